@@ -1,0 +1,115 @@
+"""Exact optimum and lower bound for the replica-placement problem (test infrastructure).
+
+The problem, as the UltraEP article states it (section on the key designs):
+every rank owns a fixed number of spare slots that may hold copies of hot
+experts, and the load (token count) of each expert is split into per-instance
+quotas; the aim is the smallest possible load on the most loaded rank.
+
+For one fixed placement, the smallest achievable maximum is a transportation
+problem: expert e ships load[e] units to the ranks hosting one of its
+instances, and every rank takes at most lam units.  By the supply-demand
+(Gale / Hall) theorem lam is feasible iff for every set X of experts
+load(X) <= lam * |N(X)|, where N(X) is the set of ranks hosting any instance
+of an expert in X; since max-flow has integral solutions, the integer optimum
+is max over X of ceil(load(X) / |N(X)|).  Enumerating every placement of the
+spare slots (each spare slot empty or holding any expert not already on its
+rank) gives the exact optimum for tiny instances.
+"""
+from __future__ import annotations
+
+import itertools
+from typing import Sequence
+
+import numpy as np
+
+
+def placement_optimum(load: Sequence[int], expert_ranks: Sequence[int]) -> int:
+    """min over integer quotas of the max rank load; expert_ranks[e] = bitmask of ranks hosting e."""
+    load = np.asarray(load, dtype=np.int64)
+    E = load.size
+    subsets = np.arange(1, 1 << E, dtype=np.int64)
+    lx = np.zeros(subsets.size, np.int64)
+    nx = np.zeros(subsets.size, np.int64)
+    for e in range(E):
+        sel = (subsets >> e) & 1
+        lx += sel * load[e]
+        nx |= sel * int(expert_ranks[e])
+    cnt = np.array([bin(int(m)).count("1") for m in nx], np.int64)
+    return int(np.max(-(-lx // cnt))) if subsets.size else 0
+
+
+def _popcount_vec(x: np.ndarray) -> np.ndarray:
+    c = np.zeros_like(x)
+    y = x.copy()
+    while np.any(y):
+        c += y & 1
+        y >>= 1
+    return c
+
+
+def brute_force_optimum(load: Sequence[int], num_ranks: int, native_rank: Sequence[int],
+                        spare_count: Sequence[int]) -> int:
+    """Exact minimum of the max rank load over every use of the spare slots.
+
+    ``native_rank[e]`` is the rank hosting expert e's native instance.  A spare
+    slot is empty or holds one expert that its rank does not host yet (a second
+    instance on one rank never lowers that rank's load).
+    """
+    load = np.asarray(load, dtype=np.int64)
+    E = load.size
+    R = num_ranks
+    base_mask = np.array([1 << int(native_rank[e]) for e in range(E)], np.int64)
+    subsets = np.arange(1, 1 << E, dtype=np.int64)
+    sel = ((subsets[:, None] >> np.arange(E)[None, :]) & 1).astype(np.int64)   # [X][E]
+    lx = sel @ load
+    native_nx = np.zeros(subsets.size, np.int64)
+    for e in range(E):
+        native_nx |= sel[:, e] * int(base_mask[e])
+    hosted = [set(int(e) for e in range(E) if native_rank[e] == r) for r in range(R)]
+
+    # choices per rank: tuples of distinct experts not native on r (order-free), size <= spare
+    per_rank = []
+    for r in range(R):
+        pool = [e for e in range(E) if e not in hosted[r]]
+        opts = []
+        for k in range(0, int(spare_count[r]) + 1):
+            opts.extend(itertools.combinations(pool, k))
+        per_rank.append(opts)
+
+    best = None
+    for choice in itertools.product(*per_rank):
+        nx = native_nx.copy()
+        for r, exps in enumerate(choice):
+            for e in exps:
+                nx |= sel[:, e] * (1 << r)
+        lam = int(np.max(-(-lx // _popcount_vec(nx))))
+        if best is None or lam < best:
+            best = lam
+    return int(best if best is not None else 0)
+
+
+def slot_lower_bound(load: Sequence[int], num_ranks: int, num_spare: int) -> int:
+    """Smallest lam >= ceil(total/R) with sum_e (ceil(load_e/lam) - 1) <= S.
+
+    Any plan with maximum rank load lam gives each instance at most lam units
+    and puts the instances of one expert on distinct ranks, so expert e needs at
+    least ceil(load_e/lam) instances, i.e. that many minus one spare slots.
+    """
+    load = np.asarray(load, dtype=np.int64)
+    total = int(load.sum())
+    if total == 0:
+        return 0
+    lo = max(-(-total // num_ranks), 1)
+    hi = max(int(load.max()), lo)
+
+    def ok(lam: int) -> bool:
+        extra = np.maximum(-(-load // lam) - 1, 0)    # an unloaded expert needs no copy
+        return int(np.sum(extra)) <= num_spare
+
+    while lo < hi:
+        mid = (lo + hi) // 2
+        if ok(mid):
+            hi = mid
+        else:
+            lo = mid + 1
+    return lo
