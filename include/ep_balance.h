@@ -1,0 +1,212 @@
+/*
+ * ep_balance.h -- real-time MoE expert load balancing on one AMD MI355X (gfx950).
+ *
+ * The calls follow the problem as the UltraEP pages state it:
+ *   - the gate emits top-k *logical* expert IDs per token; experts run as
+ *     *physical* instances: each expert's native instance plus copies placed
+ *     in a fixed number of reserved spare slots per EP rank, with no runtime
+ *     allocation (UltraEP news article, m.youleyou.com, section on the key
+ *     designs; UltraEP digest, agihunt.info, "What UltraEP does");
+ *   - balancing reads the exact load after the gate, then solves how much load
+ *     (a quota) every expert instance receives, jointly with where replicas go
+ *     (UltraEP article, key designs, control-plane paragraph);
+ *   - tokens of one logical expert are rerouted over its instances (same
+ *     section, forward-pass paragraph); the three mapping tables are those of
+ *     EPLB: physical slot -> logical expert, logical expert -> replica slots,
+ *     replica count per expert (EPLB tutorial, t6page.pages.dev, section on the
+ *     mapping tables);
+ *   - replica weights are gathered into slot buffers that every layer reuses
+ *     (UltraEP article, key designs, memory paragraph);
+ *   - imbalance = load of the most loaded rank / mean rank load (UltraEP
+ *     digest, "Reported results"); balancedness = its reciprocal (EPLB
+ *     tutorial, measured-speedup section).
+ *
+ * All EP ranks of one layer are simulated on one GPU: the rank is an array
+ * axis.  One "plan" is one (microbatch, layer); calls take P plans at once.
+ *
+ * Conventions shared by every call
+ *   - Pointers named as device data are device pointers owned by the caller;
+ *     the library allocates and frees nothing.
+ *   - Every call only enqueues work on `stream` (a hipStream_t; NULL = the
+ *     null stream) and returns; it never synchronises.  Calls on different
+ *     streams are safe when their outputs do not alias.
+ *   - The return value reports errors detectable on the host:
+ *       EP_OK, EP_ERR_INVALID_ARG (null/misaligned pointer, bad size, workspace
+ *       too small, unsupported shape), EP_ERR_HIP (a HIP runtime call failed).
+ *     Data errors found on the device never force a sync: they are reported
+ *     in the per-plan status words (EP_STATUS_*).
+ *   - Integer work throughout; results do not depend on scheduling (no
+ *     order-dependent atomics), so every output is bit-reproducible.
+ */
+#ifndef EP_BALANCE_H
+#define EP_BALANCE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void *ep_stream_t; /* a hipStream_t */
+
+enum {
+    EP_OK = 0,
+    EP_ERR_INVALID_ARG = -1,
+    EP_ERR_HIP = -2,
+};
+
+/* bits of the per-plan status word */
+enum {
+    EP_STATUS_BAD_ID = 1u,   /* an expert ID >= E was seen; such pairs count nowhere */
+    EP_STATUS_STEP_CAP = 2u, /* the planner stopped at its step cap                  */
+};
+
+/*
+ * Physical layout of one EP group: native placement + spare slots per rank.
+ *
+ * Physical slots are numbered rank-major; inside rank r the native experts come
+ * first in ascending logical ID, then the rank's spare slots.  The o-th spare
+ * slot in that order owns row o of the slot buffer.
+ *
+ * `tables` points to device memory holding ep_layout_table_ints() int32 values
+ * written by ep_layout_init(); the struct itself lives in host memory and is
+ * read by every call at enqueue time.
+ */
+typedef struct ep_layout {
+    int32_t num_experts;  /* E: logical experts                                   */
+    int32_t num_ranks;    /* R: EP ranks                                          */
+    int32_t num_phys;     /* Phi = E + S physical slots                           */
+    int32_t num_spare;    /* S: spare slots over all ranks                        */
+    int32_t max_replicas; /* rho = min(R, 1 + S): row width of log2phy            */
+    const int32_t *tables;/* device, packed tables (see ep_layout_init)           */
+} ep_layout_t;
+
+/* Number of int32 values ep_layout_init writes for (E, R, S). */
+size_t ep_layout_table_ints(int32_t num_experts, int32_t num_ranks, int32_t num_spare);
+
+/*
+ * Validate a placement, pack its tables on the host and copy them with a
+ * blocking hipMemcpy into `device_tables` (caller-owned, at least
+ * ep_layout_table_ints(E, R, sum(spare_count)) int32 values).  Fills *out.
+ *   native_count  host [R]: native experts of each rank (>= 0, sum = E)
+ *   native_experts host [E]: rank-major lists, rank r's block of native_count[r]
+ *                  IDs in any order (each logical ID exactly once)
+ *   spare_count   host [R]: spare slots of each rank (>= 0)
+ * Setup only (once per EP group), not part of the per-plan path.
+ * Returns EP_ERR_INVALID_ARG for an invalid placement or a rank count above
+ * EP_MAX_RANKS, EP_ERR_HIP if the copy fails.
+ */
+#define EP_MAX_RANKS 4096
+#define EP_MAX_EXPERTS 16384
+int ep_layout_init(int32_t num_experts, int32_t num_ranks, const int32_t *native_count,
+                   const int32_t *native_experts, const int32_t *spare_count,
+                   int32_t *device_tables, size_t device_table_ints, ep_layout_t *out);
+
+/*
+ * Workspace for one (ep_load_histogram, ep_reroute) pair, in bytes.  It carries
+ * the per-sub-block expert counts (and after the histogram, their exclusive
+ * prefix per expert) from the histogram to the reroute: pass the same buffer,
+ * untouched in between, to both.  Grows as P * ceil(N / sub-block) * (E + 1) * 4.
+ */
+size_t ep_workspace_bytes(int64_t pairs_per_plan, int32_t num_plans, int32_t num_experts);
+
+/*
+ * A1 -- exact per-expert load of every plan (UltraEP article, key designs:
+ * the global load is read after the gate and before dispatch).
+ *   topk_ids  device int32 [P][N]: N = R*T*k pairs per plan in (source rank,
+ *             token, k) order.  ID < 0 is padding (ignored); ID >= E is an
+ *             error: status bit EP_STATUS_BAD_ID, the pair is ignored.
+ *   load      device int32 [P][E] (written)
+ *   ws        device, >= ep_workspace_bytes(N, P, E) bytes, 16-byte aligned
+ *   status    device uint32 [P] (written: EP_STATUS_BAD_ID or 0)
+ * N may be 0 (loads become 0).  Requires N < 2^31, 1 <= P <= 65535.
+ */
+int ep_load_histogram(const int32_t *topk_ids, int64_t pairs_per_plan, int32_t num_plans,
+                      const ep_layout_t *layout, int32_t *load, void *ws, size_t ws_bytes,
+                      uint32_t *status, ep_stream_t stream);
+
+/*
+ * A2 -- joint replica placement and per-instance quotas, one independent plan
+ * per (microbatch, layer) starting from the native placement (UltraEP article,
+ * key designs: each exploration step may create a replica and move load; the
+ * pages do not print the solver, so the rule below is this library's reading).
+ *
+ * Greedy, capped at 2*S + R committed moves (status EP_STATUS_STEP_CAP):
+ *   h = most loaded rank (lowest index on ties); candidates = loaded instances
+ *   on h by (quota desc, expert asc).  First try to re-level a candidate that
+ *   already has replicas, else replicate one onto the least loaded rank (lowest
+ *   index on ties) that has a free spare slot and no instance of it, into that
+ *   rank's lowest free spare slot.  Every move water-fills the expert's load
+ *   over its instances: with other-expert loads b_i sorted by (b, rank), the m*
+ *   largest-prefix instances with m*b_(m) < load + sum_{j<=m} b_(j) end at
+ *   floor(S/m*) or one more (the extra units to the first S mod m* of them).
+ *   A move is kept only if it lowers h's load; the loop stops when no move
+ *   does.  Replicas left with quota 0 are freed.
+ *   load      device int32 [P][E]
+ *   phy2log   device int32 [P][Phi]: logical expert of each slot, -1 = empty
+ *   phy_quota device int32 [P][Phi]: pairs each instance receives (0 if empty)
+ *   logcnt    device int32 [P][E]: instances per expert (>= 1)
+ *   log2phy   device int32 [P][E][rho]: instance slots in ascending order, -1 padded
+ *   steps     device int32 [P] or NULL: committed moves
+ *   status    device uint32 [P] or NULL: EP_STATUS_STEP_CAP is OR-ed in
+ * Requires rho <= 64 (at most 64 instances of one expert), 1 <= P <= 65535.
+ */
+int ep_plan_quota(const int32_t *load, int32_t num_plans, const ep_layout_t *layout,
+                  int32_t *phy2log, int32_t *phy_quota, int32_t *logcnt, int32_t *log2phy,
+                  int32_t *steps, uint32_t *status, ep_stream_t stream);
+
+/*
+ * A3 -- order-preserving reroute of every (token,k) pair to a physical instance
+ * of its own logical expert (UltraEP article, key designs: reroute splits one
+ * native expert's tokens over its replicas; EPLB tutorial: the physical ID is
+ * looked up from the top-k logical ID).  The j-th pair (0-based, flat order)
+ * of expert e goes to the instance i (ascending slot order) with
+ * Q_i <= j < Q_i + quota_i, Q_i the sum of the quotas of the instances before i.
+ *   topk_ids  device int32 [P][N], the same IDs the histogram saw
+ *   phy_quota, log2phy, logcnt: a plan as ep_plan_quota writes it (each
+ *             instance a distinct slot in [0, Phi), logcnt in [0, rho])
+ *   ws        the workspace filled by ep_load_histogram for these IDs
+ *   phys_ids  device int32 [P][N] (written): physical slot, -1 for padding,
+ *             invalid IDs and pairs beyond the expert's total quota
+ */
+int ep_reroute(const int32_t *topk_ids, int64_t pairs_per_plan, int32_t num_plans,
+               const ep_layout_t *layout, const int32_t *phy_quota, const int32_t *log2phy,
+               const int32_t *logcnt, const void *ws, size_t ws_bytes, int32_t *phys_ids,
+               ep_stream_t stream);
+
+/*
+ * A4 -- weight distribution on one GPU: gather the weights of every expert that
+ * occupies a spare slot into that slot's row of the cross-layer slot buffer
+ * (UltraEP article, key designs: reserved slots, weight buffers reused across
+ * layers).  One plan (one layer) per call; empty spare slots are not written.
+ *   expert_weights device [E][bytes_per_expert], one layer (16-byte aligned)
+ *   phy2log        device int32 [Phi], that layer's plan
+ *   slot_buf       device [S][bytes_per_expert] (16-byte aligned)
+ * bytes_per_expert must be a positive multiple of 16.
+ */
+int ep_slot_fill(const void *expert_weights, int64_t bytes_per_expert, const int32_t *phy2log,
+                 const ep_layout_t *layout, void *slot_buf, ep_stream_t stream);
+
+/*
+ * A5 -- balance statistics per plan (UltraEP digest, "Reported results":
+ * most loaded rank over the mean).
+ *   stats      device int64 [P][4]: max rank load before (native placement),
+ *              max rank load after (sum of quotas per rank), total load,
+ *              replicas in use (spare slots with a positive quota)
+ *   imbalance  device double [P][2]: before, after = max * R / total (exactly
+ *              rounded; 1.0 when total == 0)
+ *   rank_load  device int32 [P][2][R] or NULL: per-rank loads before / after
+ */
+int ep_balance_stats(const int32_t *load, const int32_t *phy_quota, int32_t num_plans,
+                     const ep_layout_t *layout, int64_t *stats, double *imbalance,
+                     int32_t *rank_load, ep_stream_t stream);
+
+/* Human-readable name of a return code. */
+const char *ep_status_string(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EP_BALANCE_H */

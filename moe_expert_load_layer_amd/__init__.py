@@ -1,0 +1,245 @@
+"""Python binding of the gfx950 HIP library ``libepbalance.so`` (C ABI in include/ep_balance.h).
+
+Argument marshalling only: torch supplies device memory and the current HIP
+stream; every step runs in the library's kernels.  Function names match the C
+entry points.  Importing this module does not touch the GPU; the first call
+loads the library and raises :class:`EPBalanceError` if it is missing (no CPU
+fallback exists).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libepbalance.so")
+
+EP_OK = 0
+EP_ERR_INVALID_ARG = -1
+EP_ERR_HIP = -2
+EP_STATUS_BAD_ID = 1
+EP_STATUS_STEP_CAP = 2
+
+
+class EPBalanceError(RuntimeError):
+    pass
+
+
+class _CLayout(ctypes.Structure):
+    _fields_ = [
+        ("num_experts", ctypes.c_int32),
+        ("num_ranks", ctypes.c_int32),
+        ("num_phys", ctypes.c_int32),
+        ("num_spare", ctypes.c_int32),
+        ("max_replicas", ctypes.c_int32),
+        ("tables", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise EPBalanceError(
+                f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        lp = ctypes.POINTER(_CLayout)
+        L.ep_layout_table_ints.argtypes = [i32, i32, i32]
+        L.ep_layout_table_ints.restype = sz
+        L.ep_layout_init.argtypes = [i32, i32, vp, vp, vp, vp, sz, lp]
+        L.ep_workspace_bytes.argtypes = [i64, i32, i32]
+        L.ep_workspace_bytes.restype = sz
+        L.ep_load_histogram.argtypes = [vp, i64, i32, lp, vp, vp, sz, vp, vp]
+        L.ep_plan_quota.argtypes = [vp, i32, lp, vp, vp, vp, vp, vp, vp, vp]
+        L.ep_reroute.argtypes = [vp, i64, i32, lp, vp, vp, vp, vp, sz, vp, vp]
+        L.ep_slot_fill.argtypes = [vp, i64, vp, lp, vp, vp]
+        L.ep_balance_stats.argtypes = [vp, vp, i32, lp, vp, vp, vp, vp]
+        L.ep_status_string.argtypes = [ctypes.c_int]
+        L.ep_status_string.restype = ctypes.c_char_p
+        for f in ("ep_layout_init", "ep_load_histogram", "ep_plan_quota", "ep_reroute",
+                  "ep_slot_fill", "ep_balance_stats"):
+            getattr(L, f).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != EP_OK:
+        raise EPBalanceError(f"{what}: {lib().ep_status_string(rc).decode()} ({rc})")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t: torch.Tensor, dtype: torch.dtype, name: str) -> torch.Tensor:
+    if not t.is_cuda:
+        raise EPBalanceError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise EPBalanceError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise EPBalanceError(f"{name} must be contiguous")
+    return t
+
+
+def _stream(stream: Optional[torch.cuda.Stream]):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+@dataclass
+class Layout:
+    """Native placement + spare slots of one EP group, with its device tables."""
+
+    num_experts: int
+    num_ranks: int
+    num_phys: int
+    num_spare: int
+    max_replicas: int
+    tables: torch.Tensor
+    c: _CLayout
+
+    @classmethod
+    def create(cls, num_experts: int, native_count: Sequence[int], native_experts: Sequence[int],
+               spare_count: Sequence[int], device="cuda") -> "Layout":
+        R = len(native_count)
+        nc = (ctypes.c_int32 * R)(*[int(x) for x in native_count])
+        ne = (ctypes.c_int32 * len(native_experts))(*[int(x) for x in native_experts])
+        sc = (ctypes.c_int32 * R)(*[int(x) for x in spare_count])
+        S = int(sum(int(x) for x in spare_count))
+        n = lib().ep_layout_table_ints(num_experts, R, S)
+        if n == 0:
+            raise EPBalanceError("invalid layout sizes")
+        tables = torch.empty(n, dtype=torch.int32, device=device)
+        c = _CLayout()
+        rc = lib().ep_layout_init(num_experts, R, ctypes.cast(nc, ctypes.c_void_p),
+                                  ctypes.cast(ne, ctypes.c_void_p), ctypes.cast(sc, ctypes.c_void_p),
+                                  _ptr(tables), n, ctypes.byref(c))
+        _check(rc, "ep_layout_init")
+        return cls(c.num_experts, c.num_ranks, c.num_phys, c.num_spare, c.max_replicas, tables, c)
+
+    @classmethod
+    def from_workload(cls, wl, device="cuda") -> "Layout":
+        return cls.create(wl.num_experts, wl.native_count, list(wl.native_experts()), wl.spare_count,
+                          device)
+
+    def ref(self):
+        return ctypes.byref(self.c)
+
+
+def ep_workspace_bytes(pairs_per_plan: int, num_plans: int, num_experts: int) -> int:
+    return int(lib().ep_workspace_bytes(pairs_per_plan, num_plans, num_experts))
+
+
+def workspace(topk_ids: torch.Tensor, layout: Layout) -> torch.Tensor:
+    P, N = topk_ids.shape
+    nbytes = ep_workspace_bytes(N, P, layout.num_experts)
+    return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=topk_ids.device)
+
+
+def ep_load_histogram(topk_ids: torch.Tensor, layout: Layout, load=None, ws=None, status=None,
+                      stream=None):
+    """topk_ids int32 [P][N] -> (load int32 [P][E], ws, status uint32-as-int32 [P])."""
+    _dev(topk_ids, torch.int32, "topk_ids")
+    P, N = topk_ids.shape
+    dev = topk_ids.device
+    load = torch.empty((P, layout.num_experts), dtype=torch.int32, device=dev) if load is None else load
+    ws = workspace(topk_ids, layout) if ws is None else ws
+    status = torch.empty(P, dtype=torch.int32, device=dev) if status is None else status
+    _dev(load, torch.int32, "load"); _dev(status, torch.int32, "status")
+    rc = lib().ep_load_histogram(_ptr(topk_ids), N, P, layout.ref(), _ptr(load), _ptr(ws),
+                                 ws.numel() * ws.element_size(), _ptr(status), _stream(stream))
+    _check(rc, "ep_load_histogram")
+    return load, ws, status
+
+
+@dataclass
+class PlanOut:
+    phy2log: torch.Tensor    # int32 [P][Phi]
+    phy_quota: torch.Tensor  # int32 [P][Phi]
+    logcnt: torch.Tensor     # int32 [P][E]
+    log2phy: torch.Tensor    # int32 [P][E][rho]
+    steps: torch.Tensor      # int32 [P]
+
+
+def alloc_plan(P: int, layout: Layout, device) -> PlanOut:
+    E, Phi, rho = layout.num_experts, layout.num_phys, layout.max_replicas
+    return PlanOut(torch.empty((P, Phi), dtype=torch.int32, device=device),
+                   torch.empty((P, Phi), dtype=torch.int32, device=device),
+                   torch.empty((P, E), dtype=torch.int32, device=device),
+                   torch.empty((P, E, rho), dtype=torch.int32, device=device),
+                   torch.empty(P, dtype=torch.int32, device=device))
+
+
+def ep_plan_quota(load: torch.Tensor, layout: Layout, out: Optional[PlanOut] = None, status=None,
+                  stream=None) -> PlanOut:
+    _dev(load, torch.int32, "load")
+    P = load.shape[0]
+    out = alloc_plan(P, layout, load.device) if out is None else out
+    rc = lib().ep_plan_quota(_ptr(load), P, layout.ref(), _ptr(out.phy2log), _ptr(out.phy_quota),
+                             _ptr(out.logcnt), _ptr(out.log2phy), _ptr(out.steps), _ptr(status),
+                             _stream(stream))
+    _check(rc, "ep_plan_quota")
+    return out
+
+
+def ep_reroute(topk_ids: torch.Tensor, layout: Layout, phy_quota: torch.Tensor, log2phy: torch.Tensor,
+               logcnt: torch.Tensor, ws: torch.Tensor, phys_ids=None, stream=None) -> torch.Tensor:
+    _dev(topk_ids, torch.int32, "topk_ids")
+    for t, n in ((phy_quota, "phy_quota"), (log2phy, "log2phy"), (logcnt, "logcnt")):
+        _dev(t, torch.int32, n)
+    P, N = topk_ids.shape
+    phys_ids = torch.empty_like(topk_ids) if phys_ids is None else phys_ids
+    rc = lib().ep_reroute(_ptr(topk_ids), N, P, layout.ref(), _ptr(phy_quota), _ptr(log2phy),
+                          _ptr(logcnt), _ptr(ws), ws.numel() * ws.element_size(), _ptr(phys_ids),
+                          _stream(stream))
+    _check(rc, "ep_reroute")
+    return phys_ids
+
+
+def ep_slot_fill(expert_weights: torch.Tensor, phy2log: torch.Tensor, layout: Layout,
+                 slot_buf: torch.Tensor, stream=None) -> torch.Tensor:
+    """expert_weights [E][...] (one layer), phy2log int32 [Phi] (one plan), slot_buf [S][...]."""
+    if not (expert_weights.is_cuda and slot_buf.is_cuda and expert_weights.is_contiguous()
+            and slot_buf.is_contiguous()):
+        raise EPBalanceError("weights and slot buffer must be contiguous device tensors")
+    _dev(phy2log, torch.int32, "phy2log")
+    bpe = expert_weights.numel() * expert_weights.element_size() // layout.num_experts
+    rc = lib().ep_slot_fill(_ptr(expert_weights), bpe, _ptr(phy2log), layout.ref(), _ptr(slot_buf),
+                            _stream(stream))
+    _check(rc, "ep_slot_fill")
+    return slot_buf
+
+
+def ep_balance_stats(load: torch.Tensor, phy_quota: torch.Tensor, layout: Layout, stats=None,
+                     imbalance=None, rank_load=None, want_rank_load=True, stream=None):
+    """-> (stats int64 [P][4], imbalance float64 [P][2], rank_load int32 [P][2][R] or None)."""
+    _dev(load, torch.int32, "load"); _dev(phy_quota, torch.int32, "phy_quota")
+    P = load.shape[0]
+    dev = load.device
+    stats = torch.empty((P, 4), dtype=torch.int64, device=dev) if stats is None else stats
+    imbalance = torch.empty((P, 2), dtype=torch.float64, device=dev) if imbalance is None else imbalance
+    if rank_load is None and want_rank_load:
+        rank_load = torch.empty((P, 2, layout.num_ranks), dtype=torch.int32, device=dev)
+    rc = lib().ep_balance_stats(_ptr(load), _ptr(phy_quota), P, layout.ref(), _ptr(stats),
+                                _ptr(imbalance), _ptr(rank_load), _stream(stream))
+    _check(rc, "ep_balance_stats")
+    return stats, imbalance, rank_load
+
+
+def run_path(topk_ids: torch.Tensor, layout: Layout, stream=None):
+    """hist -> plan -> reroute -> stats for a batch of plans; returns a dict of device tensors."""
+    load, ws, status = ep_load_histogram(topk_ids, layout, stream=stream)
+    plan = ep_plan_quota(load, layout, status=status, stream=stream)
+    phys = ep_reroute(topk_ids, layout, plan.phy_quota, plan.log2phy, plan.logcnt, ws, stream=stream)
+    stats, imb, rank_load = ep_balance_stats(load, plan.phy_quota, layout, stream=stream)
+    return dict(load=load, ws=ws, status=status, plan=plan, phys=phys, stats=stats, imbalance=imb,
+                rank_load=rank_load)

@@ -1,0 +1,190 @@
+// C-ABI entry points: argument checks on the host, then kernel launches on the
+// caller's stream.  No allocation, no synchronisation (except the one-time
+// blocking copy in ep_layout_init).
+#include <stdlib.h>
+#include <string.h>
+
+#include <vector>
+
+#include "ep_internal.h"
+
+using namespace ep;
+
+namespace {
+
+constexpr size_t kMaxLds = 65536;
+constexpr int64_t kMaxPairs = 0x7fffffffLL;
+constexpr int32_t kMaxPlans = 65535;
+
+inline hipStream_t as_stream(ep_stream_t s) { return reinterpret_cast<hipStream_t>(s); }
+inline bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+inline int hip_rc(hipError_t e) { return e == hipSuccess ? EP_OK : EP_ERR_HIP; }
+
+bool layout_ok(const ep_layout_t *L) {
+    if (!L || !L->tables) return false;
+    if (L->num_experts < 1 || L->num_experts > EP_MAX_EXPERTS) return false;
+    if (L->num_ranks < 1 || L->num_ranks > EP_MAX_RANKS) return false;
+    if (L->num_spare < 0 || L->num_phys != L->num_experts + L->num_spare) return false;
+    const int32_t rho = L->num_ranks < 1 + L->num_spare ? L->num_ranks : 1 + L->num_spare;
+    if (L->max_replicas != rho) return false;
+    return aligned(L->tables, 4);
+}
+
+bool pairs_ok(const int32_t *ids, int64_t N, int32_t P) {
+    if (N < 0 || N > kMaxPairs || P < 1 || P > kMaxPlans) return false;
+    if (N > 0 && (!ids || !aligned(ids, 4))) return false;
+    return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ep_layout_table_ints(int32_t num_experts, int32_t num_ranks, int32_t num_spare) {
+    if (num_experts < 1 || num_ranks < 1 || num_spare < 0) return 0;
+    return table_ints(num_experts, num_ranks, num_spare);
+}
+
+int ep_layout_init(int32_t E, int32_t R, const int32_t *native_count, const int32_t *native_experts,
+                   const int32_t *spare_count, int32_t *device_tables, size_t device_table_ints,
+                   ep_layout_t *out) {
+    if (!native_count || !native_experts || !spare_count || !device_tables || !out)
+        return EP_ERR_INVALID_ARG;
+    if (E < 1 || E > EP_MAX_EXPERTS || R < 1 || R > EP_MAX_RANKS || !aligned(device_tables, 4))
+        return EP_ERR_INVALID_ARG;
+    int64_t nat_total = 0, S = 0;
+    for (int r = 0; r < R; r++) {
+        if (native_count[r] < 0 || spare_count[r] < 0) return EP_ERR_INVALID_ARG;
+        nat_total += native_count[r];
+        S += spare_count[r];
+    }
+    if (nat_total != E || S > (int64_t)EP_MAX_EXPERTS * 64) return EP_ERR_INVALID_ARG;
+    const int Phi = E + (int)S;
+    const size_t need = table_ints(E, R, (int)S);
+    if (device_table_ints < need) return EP_ERR_INVALID_ARG;
+
+    std::vector<int32_t> t(need);
+    int32_t *rank_first = t.data();
+    int32_t *rank_nat = rank_first + R + 1;
+    int32_t *slot_home = rank_nat + R;
+    int32_t *slot_rank = slot_home + Phi;
+    int32_t *home_slot = slot_rank + Phi;
+    int32_t *spare_slot = home_slot + E;
+    for (int e = 0; e < E; e++) home_slot[e] = -1;
+    int slot = 0, in = 0, o = 0;
+    std::vector<int32_t> blk;
+    for (int r = 0; r < R; r++) {
+        rank_first[r] = slot;
+        rank_nat[r] = native_count[r];
+        blk.assign(native_experts + in, native_experts + in + native_count[r]);
+        in += native_count[r];
+        // natives of a rank in ascending logical ID (counting over the ID range
+        // would cost O(E) per rank; a small insertion sort is enough here)
+        for (size_t i = 1; i < blk.size(); i++)
+            for (size_t j = i; j > 0 && blk[j - 1] > blk[j]; j--) {
+                const int32_t x = blk[j];
+                blk[j] = blk[j - 1];
+                blk[j - 1] = x;
+            }
+        for (int32_t e : blk) {
+            if (e < 0 || e >= E || home_slot[e] != -1) return EP_ERR_INVALID_ARG;
+            home_slot[e] = slot;
+            slot_home[slot] = e;
+            slot_rank[slot] = r;
+            slot++;
+        }
+        for (int i = 0; i < spare_count[r]; i++) {
+            slot_home[slot] = -1;
+            slot_rank[slot] = r;
+            spare_slot[o++] = slot;
+            slot++;
+        }
+    }
+    rank_first[R] = slot;
+    if (hipMemcpy(device_tables, t.data(), need * sizeof(int32_t), hipMemcpyHostToDevice) != hipSuccess)
+        return EP_ERR_HIP;
+    out->num_experts = E;
+    out->num_ranks = R;
+    out->num_phys = Phi;
+    out->num_spare = (int32_t)S;
+    out->max_replicas = R < 1 + (int32_t)S ? R : 1 + (int32_t)S;
+    out->tables = device_tables;
+    return EP_OK;
+}
+
+size_t ep_workspace_bytes(int64_t pairs_per_plan, int32_t num_plans, int32_t num_experts) {
+    if (pairs_per_plan < 0 || num_plans < 1 || num_experts < 1) return 0;
+    return ws_bytes(pairs_per_plan, num_plans, num_experts);
+}
+
+int ep_load_histogram(const int32_t *topk_ids, int64_t N, int32_t P, const ep_layout_t *layout,
+                      int32_t *load, void *ws, size_t ws_size, uint32_t *status,
+                      ep_stream_t stream) {
+    if (!layout_ok(layout) || !pairs_ok(topk_ids, N, P) || !load || !status) return EP_ERR_INVALID_ARG;
+    const int E = layout->num_experts;
+    if ((size_t)4 * (E + 1) * 4 > kMaxLds) return EP_ERR_INVALID_ARG;
+    const size_t need = ws_bytes(N, P, E);
+    if (ws_size < need || (need > 0 && (!ws || !aligned(ws, 16)))) return EP_ERR_INVALID_ARG;
+    const int64_t sub = sub_pairs(N, P, E);
+    return hip_rc(launch_histogram(topk_ids, N, P, E, sub, num_sub(N, sub),
+                                   static_cast<int32_t *>(ws), load, status, as_stream(stream)));
+}
+
+int ep_plan_quota(const int32_t *load, int32_t P, const ep_layout_t *layout, int32_t *phy2log,
+                  int32_t *phy_quota, int32_t *logcnt, int32_t *log2phy, int32_t *steps,
+                  uint32_t *status, ep_stream_t stream) {
+    if (!layout_ok(layout) || !load || !phy2log || !phy_quota || !logcnt || !log2phy)
+        return EP_ERR_INVALID_ARG;
+    if (P < 1 || P > kMaxPlans || layout->max_replicas > 64) return EP_ERR_INVALID_ARG;
+    if (plan_lds_bytes(*layout) > kMaxLds) return EP_ERR_INVALID_ARG;
+    return hip_rc(launch_plan(load, P, *layout, phy2log, phy_quota, logcnt, log2phy, steps, status,
+                              as_stream(stream)));
+}
+
+int ep_reroute(const int32_t *topk_ids, int64_t N, int32_t P, const ep_layout_t *layout,
+               const int32_t *phy_quota, const int32_t *log2phy, const int32_t *logcnt,
+               const void *ws, size_t ws_size, int32_t *phys_ids, ep_stream_t stream) {
+    if (!layout_ok(layout) || !pairs_ok(topk_ids, N, P) || !phy_quota || !log2phy || !logcnt)
+        return EP_ERR_INVALID_ARG;
+    if (N > 0 && (!phys_ids || !aligned(phys_ids, 4))) return EP_ERR_INVALID_ARG;
+    const int E = layout->num_experts;
+    if (reroute_lds_bytes(E, layout->num_phys, 1) > kMaxLds) return EP_ERR_INVALID_ARG;
+    const size_t need = ws_bytes(N, P, E);
+    if (ws_size < need || (need > 0 && (!ws || !aligned(ws, 16)))) return EP_ERR_INVALID_ARG;
+    const int64_t sub = sub_pairs(N, P, E);
+    return hip_rc(launch_reroute(topk_ids, N, P, *layout, sub, num_sub(N, sub),
+                                 static_cast<const int32_t *>(ws), phy_quota, log2phy, logcnt,
+                                 phys_ids, as_stream(stream)));
+}
+
+int ep_slot_fill(const void *expert_weights, int64_t bytes_per_expert, const int32_t *phy2log,
+                 const ep_layout_t *layout, void *slot_buf, ep_stream_t stream) {
+    if (!layout_ok(layout) || !phy2log || bytes_per_expert <= 0 || bytes_per_expert % 16 != 0)
+        return EP_ERR_INVALID_ARG;
+    if (layout->num_spare == 0) return EP_OK;
+    if (!expert_weights || !slot_buf || !aligned(expert_weights, 16) || !aligned(slot_buf, 16))
+        return EP_ERR_INVALID_ARG;
+    if (layout->num_spare > kMaxPlans) return EP_ERR_INVALID_ARG;
+    return hip_rc(launch_slot_fill(expert_weights, bytes_per_expert, phy2log, *layout, slot_buf,
+                                   as_stream(stream)));
+}
+
+int ep_balance_stats(const int32_t *load, const int32_t *phy_quota, int32_t P,
+                     const ep_layout_t *layout, int64_t *stats, double *imbalance,
+                     int32_t *rank_load, ep_stream_t stream) {
+    if (!layout_ok(layout) || !load || !phy_quota || !stats || !imbalance) return EP_ERR_INVALID_ARG;
+    if (P < 1 || P > kMaxPlans || !aligned(stats, 8) || !aligned(imbalance, 8)) return EP_ERR_INVALID_ARG;
+    return hip_rc(launch_stats(load, phy_quota, P, *layout, stats, imbalance, rank_load,
+                               as_stream(stream)));
+}
+
+const char *ep_status_string(int code) {
+    switch (code) {
+        case EP_OK: return "EP_OK";
+        case EP_ERR_INVALID_ARG: return "EP_ERR_INVALID_ARG";
+        case EP_ERR_HIP: return "EP_ERR_HIP";
+        default: return "EP_UNKNOWN";
+    }
+}
+
+}  // extern "C"

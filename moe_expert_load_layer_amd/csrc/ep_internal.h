@@ -1,0 +1,167 @@
+// Internal definitions shared by the HIP kernels and the C-ABI entry points.
+// gfx950 (CDNA4) only: wave64, LDS atomics, 16-byte global accesses.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/ep_balance.h"
+
+namespace ep {
+
+constexpr int kWave = 64;
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// Packed layout tables (int32, device), in this order:
+//   rank_first [R+1]  first physical slot of each rank (rank-major numbering)
+//   rank_nat   [R]    native slots at the start of each rank
+//   slot_home  [Phi]  native expert of a slot, -1 for a spare slot
+//   slot_rank  [Phi]  rank owning a slot
+//   home_slot  [E]    native slot of each expert
+//   spare_slot [S]    physical slot of the o-th spare slot (ascending)
+// ---------------------------------------------------------------------------
+struct Tables {
+    const int32_t *rank_first, *rank_nat, *slot_home, *slot_rank, *home_slot, *spare_slot;
+};
+
+inline size_t table_ints(int E, int R, int S) {
+    return (size_t)(2 * R + 1) + 2 * (size_t)(E + S) + (size_t)E + (size_t)S;
+}
+
+inline Tables tables_of(const ep_layout_t &L) {
+    const int R = L.num_ranks, Phi = L.num_phys, E = L.num_experts;
+    Tables t;
+    t.rank_first = L.tables;
+    t.rank_nat = t.rank_first + (R + 1);
+    t.slot_home = t.rank_nat + R;
+    t.slot_rank = t.slot_home + Phi;
+    t.home_slot = t.slot_rank + Phi;
+    t.spare_slot = t.home_slot + E;
+    return t;
+}
+
+// ---------------------------------------------------------------------------
+// Sub-blocks: the pairs of one plan are cut into consecutive sub-blocks, one
+// per wave, in both the histogram and the reroute.  The histogram stores each
+// sub-block's expert counts (plus a count of invalid IDs in column E); the
+// scan turns them into exclusive per-expert offsets.  The size aims at ~8K
+// waves in a launch, keeps the count table under 1/4 byte per pair
+// (>= 16 (E+1) pairs), and is a power of two between 2048 and 32768.
+// ---------------------------------------------------------------------------
+inline int64_t sub_pairs(int64_t N, int32_t P, int32_t E) {
+    int64_t want = (N * (int64_t)P + 8191) / 8192;
+    int64_t lo = 16 * (int64_t)(E + 1);
+    if (lo < 2048) lo = 2048;
+    if (want < lo) want = lo;
+    int64_t sub = 2048;
+    while (sub < want && sub < 32768) sub <<= 1;
+    while (sub < lo) sub <<= 1;
+    return sub;
+}
+
+inline int64_t num_sub(int64_t N, int64_t sub) { return N <= 0 ? 0 : (N + sub - 1) / sub; }
+
+inline size_t ws_bytes(int64_t N, int32_t P, int32_t E) {
+    const int64_t sub = sub_pairs(N, P, E);
+    return (size_t)P * (size_t)num_sub(N, sub) * (size_t)(E + 1) * sizeof(int32_t);
+}
+
+// ---------------------------------------------------------------------------
+// wave64 primitives
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int lane_id() {
+    return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+}
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+    const int l = lane_id();
+    return l == 0 ? 0ull : (~0ull >> (64 - l));
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+    const uint32_t lo = __shfl_xor((unsigned)(v & 0xffffffffu), m);
+    const uint32_t hi = __shfl_xor((unsigned)(v >> 32), m);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ int64_t shfl_up_i64(int64_t v, int d) {
+    const uint64_t u = (uint64_t)v;
+    const uint32_t lo = __shfl_up((unsigned)(u & 0xffffffffu), d);
+    const uint32_t hi = __shfl_up((unsigned)(u >> 32), d);
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+    for (int m = 32; m > 0; m >>= 1) {
+        const uint64_t o = shfl_xor_u64(v, m);
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
+__device__ __forceinline__ int wave_sum_i32(int v) {
+#pragma unroll
+    for (int m = 32; m > 0; m >>= 1) v += __shfl_xor(v, m);
+    return v;
+}
+
+// inclusive prefix sum over the 64 lanes
+__device__ __forceinline__ int64_t wave_incl_scan_i64(int64_t v) {
+    const int l = lane_id();
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int64_t o = shfl_up_i64(v, d);
+        if (l >= d) v += o;
+    }
+    return v;
+}
+
+__device__ __forceinline__ int wave_incl_scan_i32(int v) {
+    const int l = lane_id();
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int o = __shfl_up(v, d);
+        if (l >= d) v += o;
+    }
+    return v;
+}
+
+__device__ __forceinline__ int64_t readlane_i64(int64_t v, int lane) {
+    const uint64_t u = (uint64_t)v;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(u & 0xffffffffu), lane);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(u >> 32), lane);
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// orders LDS accesses of the lanes of one wave (no workgroup barrier)
+__device__ __forceinline__ void wave_lds_fence() {
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
+
+// ---------------------------------------------------------------------------
+// launchers (defined in the .hip files; return hipError_t of the launch)
+// ---------------------------------------------------------------------------
+hipError_t launch_histogram(const int32_t *ids, int64_t N, int32_t P, int32_t E, int64_t sub,
+                            int64_t nsb, int32_t *ws, int32_t *load, uint32_t *status,
+                            hipStream_t s);
+hipError_t launch_plan(const int32_t *load, int32_t P, const ep_layout_t &L, int32_t *phy2log,
+                       int32_t *phy_quota, int32_t *logcnt, int32_t *log2phy, int32_t *steps,
+                       uint32_t *status, hipStream_t s);
+size_t plan_lds_bytes(const ep_layout_t &L);
+hipError_t launch_reroute(const int32_t *ids, int64_t N, int32_t P, const ep_layout_t &L,
+                          int64_t sub, int64_t nsb, const int32_t *ws, const int32_t *phy_quota,
+                          const int32_t *log2phy, const int32_t *logcnt, int32_t *out,
+                          hipStream_t s);
+size_t reroute_lds_bytes(int E, int Phi, int waves);
+hipError_t launch_slot_fill(const void *w, int64_t bytes_per_expert, const int32_t *phy2log,
+                            const ep_layout_t &L, void *buf, hipStream_t s);
+hipError_t launch_stats(const int32_t *load, const int32_t *phy_quota, int32_t P,
+                        const ep_layout_t &L, int64_t *stats, double *imbalance,
+                        int32_t *rank_load, hipStream_t s);
+
+}  // namespace ep

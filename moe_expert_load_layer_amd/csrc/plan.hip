@@ -1,0 +1,275 @@
+// A2: joint replica placement + per-instance quotas (UltraEP news article,
+// section on the key designs: the solver works out how much load each expert
+// instance receives, and each exploration step may both instantiate a replica
+// and update the load distribution; the load lives in fixed spare slots).
+//
+// One wave (one workgroup of 64 lanes) per plan; plans of many layers and
+// microbatches run side by side in one launch.  All state sits in LDS:
+//   rank loads, free spare counts, slot owners and quotas, per-expert
+//   instance counts.
+// Each step:
+//   1. hottest rank h   = wave max of the packed key (load << 32 | ~rank);
+//   2. candidates       = loaded instances on h, visited in descending
+//                         (quota << 32 | ~expert) order by repeated wave max;
+//   3. re-level pass    (experts that already have a replica), then a
+//      replicate pass   (destination = wave max of (~load << 32 | ~rank) over
+//                         ranks with a free spare and no instance of the expert);
+//   4. water-fill       of the expert's load over its instances: instances sit
+//                         one per lane, are ranked by (background, rank) with a
+//                         64-way count, the sorted backgrounds go through a wave
+//                         prefix sum, and a ballot finds the filled prefix m*.
+// A move is committed only when it lowers h's load.  Integer arithmetic only.
+#include "ep_internal.h"
+
+namespace ep {
+namespace {
+
+struct PlanArgs {
+    int32_t E, R, Phi, S, rho;
+    Tables T;
+};
+
+__device__ __forceinline__ uint32_t inv(uint32_t x) { return 0xffffffffu - x; }
+
+__global__ __launch_bounds__(kWave) void plan_kernel(const int32_t *__restrict__ load, PlanArgs a,
+                                                     int32_t *__restrict__ phy2log,
+                                                     int32_t *__restrict__ phy_quota,
+                                                     int32_t *__restrict__ logcnt,
+                                                     int32_t *__restrict__ log2phy,
+                                                     int32_t *__restrict__ steps_out,
+                                                     uint32_t *__restrict__ status) {
+    const int E = a.E, R = a.R, Phi = a.Phi, S = a.S, rho = a.rho;
+    extern __shared__ __align__(16) unsigned char sh_raw[];
+    uint64_t *emask = reinterpret_cast<uint64_t *>(sh_raw);  // [E]
+    int64_t *sbuf = reinterpret_cast<int64_t *>(emask + E);  // [64]
+    int32_t *rl = reinterpret_cast<int32_t *>(sbuf + kWave);  // [R]  rank load
+    int32_t *freec = rl + R;                                   // [R]  free spare slots
+    int32_t *rfirst = freec + R;                               // [R+1]
+    int32_t *rnat = rfirst + R + 1;                            // [R]
+    int32_t *stamp = rnat + R;                                 // [R]
+    int32_t *owner = stamp + R;                                // [Phi]
+    int32_t *quota = owner + Phi;                              // [Phi]
+    int32_t *srank = quota + Phi;                              // [Phi]
+    int32_t *hslot = srank + Phi;                              // [E]
+    int32_t *ld = hslot + E;                                   // [E]
+    int32_t *icnt = ld + E;                                    // [E]
+    int32_t *erun = icnt + E;                                  // [E]
+    int32_t *nshift = erun + E;                                // [E]
+    int32_t *sslot = nshift + E;                               // [S]
+    int32_t *islot = sslot + S;                                // [64]
+
+    const int p = blockIdx.x;
+    const int lane = threadIdx.x;
+    const int32_t *lp = load + (int64_t)p * E;
+
+    for (int r = lane; r <= R; r += kWave) rfirst[r] = a.T.rank_first[r];
+    for (int r = lane; r < R; r += kWave) { rnat[r] = a.T.rank_nat[r]; stamp[r] = -1; }
+    for (int s = lane; s < Phi; s += kWave) { owner[s] = a.T.slot_home[s]; srank[s] = a.T.slot_rank[s]; }
+    for (int e = lane; e < E; e += kWave) { hslot[e] = a.T.home_slot[e]; ld[e] = lp[e]; icnt[e] = 1; }
+    for (int o = lane; o < S; o += kWave) sslot[o] = a.T.spare_slot[o];
+    __syncthreads();
+    for (int s = lane; s < Phi; s += kWave) {
+        const int e = owner[s];
+        quota[s] = e >= 0 ? ld[e] : 0;
+    }
+    __syncthreads();
+    for (int r = lane; r < R; r += kWave) {
+        int sum = 0;
+        for (int s = rfirst[r]; s < rfirst[r + 1]; s++) sum += quota[s];
+        rl[r] = sum;
+        freec[r] = rfirst[r + 1] - rfirst[r] - rnat[r];
+    }
+    __syncthreads();
+
+    int tries = 0;
+    const uint64_t lt = lanemask_lt();
+
+    // Water-fill expert e over its instances (plus a new one on the least loaded
+    // eligible rank when `replicate`); commit if h's load drops below Lh.
+    auto try_move = [&](int e, bool replicate, int h, int64_t Lh) -> bool {
+        // instances: native in lane 0, replicas compacted after it
+        if (lane == 0) islot[0] = hslot[e];
+        int n = 1;
+        for (int base = 0; base < S; base += kWave) {
+            const int o = base + lane;
+            int s = -1;
+            bool own = false;
+            if (o < S) { s = sslot[o]; own = owner[s] == e; }
+            const uint64_t m = __ballot(own);
+            if (own) islot[n + __popcll(m & lt)] = s;
+            n += __popcll(m);
+        }
+        __syncthreads();
+        int d = -1;
+        if (replicate) {
+            tries++;
+            if (lane < n) stamp[srank[islot[lane]]] = tries;
+            __syncthreads();
+            uint64_t best = 0;
+            for (int r = lane; r < R; r += kWave) {
+                if (freec[r] > 0 && stamp[r] != tries) {
+                    const uint64_t k = ((uint64_t)inv((uint32_t)rl[r]) << 32) | inv((uint32_t)r);
+                    best = k > best ? k : best;
+                }
+            }
+            best = wave_max_u64(best);
+            if (best == 0) return false;
+            d = (int)inv((uint32_t)best);
+            n += 1;
+        }
+        int my_r = 0, my_q = 0, my_s = -1;
+        if (lane < n) {
+            if (replicate && lane == n - 1) {
+                my_r = d;
+                my_s = rfirst[d] + rnat[d] + (rfirst[d + 1] - rfirst[d] - rnat[d] - freec[d]);
+            } else {
+                my_s = islot[lane];
+                my_r = srank[my_s];
+                my_q = quota[my_s];
+            }
+        }
+        const int64_t my_b = (lane < n) ? (int64_t)rl[my_r] - my_q : 0;
+        const uint64_t my_key = ((uint64_t)my_b << 32) | (uint32_t)my_r;
+        int pos = 0;
+        for (int j = 0; j < n; j++) {
+            const uint64_t kj = (uint64_t)readlane_i64((int64_t)my_key, j);
+            pos += kj < my_key ? 1 : 0;
+        }
+        if (lane < n) sbuf[pos] = my_b;
+        __syncthreads();
+        const int64_t bs = (lane < n) ? sbuf[lane] : 0;
+        const int64_t Sm = (int64_t)ld[e] + wave_incl_scan_i64(bs);
+        const uint64_t cm = __ballot(lane < n && (int64_t)(lane + 1) * bs < Sm);
+        const int mstar = cm ? 64 - __clzll((long long)cm) : 0;
+        int64_t base = 0, rem = 0;
+        if (mstar > 0) {
+            const int64_t Ss = readlane_i64(Sm, mstar - 1);
+            base = Ss / mstar;
+            rem = Ss - (int64_t)mstar * base;
+        }
+        int64_t my_nq = 0;
+        if (lane < n && pos < mstar) my_nq = base - my_b + (pos < rem ? 1 : 0);
+        const uint64_t hm = __ballot(lane < n && my_r == h);
+        const int hl = __ffsll((long long)hm) - 1;
+        const int64_t newLh = readlane_i64(my_b + my_nq, hl);
+        __syncthreads();
+        if (newLh >= Lh) return false;
+        if (lane < n) {
+            quota[my_s] = (int32_t)my_nq;
+            rl[my_r] = (int32_t)(my_b + my_nq);
+        }
+        if (replicate && lane == n - 1) {
+            owner[my_s] = e;
+            freec[d] -= 1;
+            icnt[e] += 1;
+        }
+        __syncthreads();
+        return true;
+    };
+
+    const int cap = 2 * S + R;
+    int steps = 0, cap_hit = 0;
+    for (;;) {
+        if (steps == cap) { cap_hit = 1; break; }
+        uint64_t key = 0;
+        for (int r = lane; r < R; r += kWave) {
+            const uint64_t k = ((uint64_t)(uint32_t)rl[r] << 32) | inv((uint32_t)r);
+            key = k > key ? k : key;
+        }
+        key = wave_max_u64(key);
+        const int h = (int)inv((uint32_t)key);
+        const int64_t Lh = (int64_t)(key >> 32);
+        const int f0 = rfirst[h], nh = rfirst[h + 1] - f0;
+
+        bool committed = false;
+        for (int pass = 0; pass < 2 && !committed; pass++) {
+            uint64_t prev = ~0ull;
+            for (;;) {
+                uint64_t best = 0;
+                for (int i = lane; i < nh; i += kWave) {
+                    const int s = f0 + i;
+                    const int e = owner[s];
+                    const int q = quota[s];
+                    if (e >= 0 && q > 0 && (pass == 1 || icnt[e] >= 2)) {
+                        const uint64_t k = ((uint64_t)(uint32_t)q << 32) | inv((uint32_t)e);
+                        if (k < prev && k > best) best = k;
+                    }
+                }
+                best = wave_max_u64(best);
+                if (best == 0) break;
+                prev = best;
+                const int e = (int)inv((uint32_t)best);
+                if (try_move(e, pass == 1, h, Lh)) { committed = true; break; }
+            }
+        }
+        if (!committed) break;
+        steps++;
+    }
+
+    // replicas left without load are freed; natives always stay
+    for (int o = lane; o < S; o += kWave) {
+        const int s = sslot[o];
+        if (owner[s] >= 0 && quota[s] == 0) owner[s] = -1;
+    }
+    for (int e = lane; e < E; e += kWave) { emask[e] = 0; erun[e] = 0; nshift[e] = 0; }
+    __syncthreads();
+
+    int32_t *o_p2l = phy2log + (int64_t)p * Phi;
+    int32_t *o_q = phy_quota + (int64_t)p * Phi;
+    for (int s = lane; s < Phi; s += kWave) { o_p2l[s] = owner[s]; o_q[s] = quota[s]; }
+    int32_t *o_l2p = log2phy + (int64_t)p * E * rho;
+    for (int64_t i = lane; i < (int64_t)E * rho; i += kWave) o_l2p[i] = -1;
+    __syncthreads();
+
+    // position of each replica among its expert's instances (ascending slots):
+    // spare slots are visited in ascending order 64 at a time; an LDS bit mask
+    // per expert gives the rank inside the group, a per-expert counter the
+    // count of earlier groups
+    for (int base = 0; base < S; base += kWave) {
+        const int o = base + lane;
+        int s = -1, e = -1;
+        if (o < S) { s = sslot[o]; e = owner[s]; }
+        if (e >= 0) atomicOr(reinterpret_cast<unsigned long long *>(&emask[e]), 1ull << lane);
+        __syncthreads();
+        uint64_t m = 0;
+        int run = 0;
+        if (e >= 0) { m = emask[e]; run = erun[e]; }
+        __syncthreads();
+        if (e >= 0) {
+            const uint64_t below = m & lt;
+            if (below == 0) { erun[e] = run + __popcll(m); emask[e] = 0; }
+            const int hs = hslot[e];
+            const int pos = run + __popcll(below) + (hs < s ? 1 : 0);
+            if (pos < rho) o_l2p[(int64_t)e * rho + pos] = s;
+            if (hs > s) atomicAdd(&nshift[e], 1);
+        }
+        __syncthreads();
+    }
+    for (int e = lane; e < E; e += kWave) {
+        const int ns = nshift[e];
+        if (ns < rho) o_l2p[(int64_t)e * rho + ns] = hslot[e];
+        logcnt[(int64_t)p * E + e] = 1 + erun[e];
+    }
+    if (lane == 0) {
+        if (steps_out) steps_out[p] = steps;
+        if (status && cap_hit) status[p] |= (uint32_t)EP_STATUS_STEP_CAP;
+    }
+}
+
+}  // namespace
+
+size_t plan_lds_bytes(const ep_layout_t &L) {
+    const size_t E = L.num_experts, R = L.num_ranks, Phi = L.num_phys, S = L.num_spare;
+    return 8 * E + 8 * kWave + 4 * (5 * R + 1 + 3 * Phi + 5 * E + S + kWave);
+}
+
+hipError_t launch_plan(const int32_t *load, int32_t P, const ep_layout_t &L, int32_t *phy2log,
+                       int32_t *phy_quota, int32_t *logcnt, int32_t *log2phy, int32_t *steps,
+                       uint32_t *status, hipStream_t s) {
+    PlanArgs a{L.num_experts, L.num_ranks, L.num_phys, L.num_spare, L.max_replicas, tables_of(L)};
+    hipLaunchKernelGGL(plan_kernel, dim3((unsigned)P), dim3(kWave), plan_lds_bytes(L), s, load, a,
+                       phy2log, phy_quota, logcnt, log2phy, steps, status);
+    return hipGetLastError();
+}
+
+}  // namespace ep

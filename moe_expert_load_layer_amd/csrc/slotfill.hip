@@ -1,0 +1,50 @@
+// A4: weight distribution on one GPU (UltraEP news article, section on the key
+// designs: replicas live in slots reserved per rank, and one slot buffer is
+// reused by every layer).  For the o-th spare slot s with phy2log[s] = e >= 0,
+// expert e's weights are copied into row o of the slot buffer; empty slots are
+// not written.  A pure HBM-to-HBM stream: 16-byte non-temporal loads and
+// stores, each workgroup moving one 64 KiB chunk of one slot.
+#include "ep_internal.h"
+
+namespace ep {
+namespace {
+
+constexpr int kFillThreads = 256;
+constexpr int kFillUnroll = 4;
+constexpr int64_t kFillChunk = (int64_t)kFillThreads * kFillUnroll * 4;  // 16-byte vectors
+
+__global__ __launch_bounds__(kFillThreads) void slot_fill_kernel(
+    const u32x4 *__restrict__ w, int64_t vpe, int32_t E, const int32_t *__restrict__ phy2log,
+    const int32_t *__restrict__ spare_slot, u32x4 *__restrict__ buf) {
+    const int o = blockIdx.y;
+    const int e = phy2log[spare_slot[o]];
+    if (e < 0 || e >= E) return;
+    const int64_t c0 = (int64_t)blockIdx.x * kFillChunk;
+    const int64_t c1 = (c0 + kFillChunk < vpe) ? c0 + kFillChunk : vpe;
+    const u32x4 *src = w + (int64_t)e * vpe;
+    u32x4 *dst = buf + (int64_t)o * vpe;
+    int64_t i = c0 + threadIdx.x;
+    for (; i + (kFillUnroll - 1) * kFillThreads < c1; i += kFillUnroll * kFillThreads) {
+        u32x4 x[kFillUnroll];
+#pragma unroll
+        for (int u = 0; u < kFillUnroll; u++) x[u] = __builtin_nontemporal_load(src + i + u * kFillThreads);
+#pragma unroll
+        for (int u = 0; u < kFillUnroll; u++) __builtin_nontemporal_store(x[u], dst + i + u * kFillThreads);
+    }
+    for (; i < c1; i += kFillThreads) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+}
+
+}  // namespace
+
+hipError_t launch_slot_fill(const void *w, int64_t bytes_per_expert, const int32_t *phy2log,
+                            const ep_layout_t &L, void *buf, hipStream_t s) {
+    if (L.num_spare == 0) return hipSuccess;
+    const int64_t vpe = bytes_per_expert / 16;
+    dim3 grid((unsigned)((vpe + kFillChunk - 1) / kFillChunk), (unsigned)L.num_spare);
+    hipLaunchKernelGGL(slot_fill_kernel, grid, dim3(kFillThreads), 0, s,
+                       reinterpret_cast<const u32x4 *>(w), vpe, L.num_experts, phy2log,
+                       tables_of(L).spare_slot, reinterpret_cast<u32x4 *>(buf));
+    return hipGetLastError();
+}
+
+}  // namespace ep

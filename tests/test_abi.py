@@ -1,0 +1,82 @@
+"""The C-ABI library loads on the CPU host and exports every entry point the
+public header declares; host-side argument checks run without a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ep_balance.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(ep_[a-z_]+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_path():
+    names = _declared()
+    for n in ("ep_load_histogram", "ep_plan_quota", "ep_reroute", "ep_slot_fill", "ep_balance_stats",
+              "ep_workspace_bytes", "ep_layout_init", "ep_layout_table_ints", "ep_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    import moe_expert_load_layer_amd as ep
+    if not os.path.exists(ep.LIB_PATH):
+        pytest.skip("library not built")
+    lib = ctypes.CDLL(ep.LIB_PATH)
+    for n in _declared():
+        assert hasattr(lib, n), n
+
+
+def test_host_side_checks_without_gpu():
+    import moe_expert_load_layer_amd as ep
+    if not os.path.exists(ep.LIB_PATH):
+        pytest.skip("library not built")
+    L = ep.lib()
+    assert L.ep_status_string(0) == b"EP_OK"
+    assert L.ep_status_string(-1) == b"EP_ERR_INVALID_ARG"
+    assert L.ep_layout_table_ints(12, 8, 4) == 2 * 8 + 1 + 2 * 16 + 12 + 4
+    assert L.ep_workspace_bytes(-1, 1, 4) == 0
+    assert L.ep_workspace_bytes(0, 3, 4) == 0
+    # workspace grows with the number of sub-blocks
+    a = L.ep_workspace_bytes(1 << 20, 1, 128)
+    b = L.ep_workspace_bytes(1 << 21, 1, 128)
+    assert 0 < a < b
+    assert a % (129 * 4) == 0
+    # null pointers are rejected before any device work
+    lay = ep._CLayout(12, 8, 16, 4, 5, None)
+    rc = L.ep_load_histogram(None, 512, 1, ctypes.byref(lay), None, None, 0, None, None)
+    assert rc == ep.EP_ERR_INVALID_ARG
+    rc = L.ep_plan_quota(None, 1, ctypes.byref(lay), None, None, None, None, None, None, None)
+    assert rc == ep.EP_ERR_INVALID_ARG
+    # inconsistent layout header (rho must be min(R, 1+S)) is rejected
+    lay_bad = ep._CLayout(12, 8, 16, 4, 4, ctypes.c_void_p(16))
+    rc = L.ep_balance_stats(ctypes.c_void_p(16), ctypes.c_void_p(16), 1, ctypes.byref(lay_bad),
+                            ctypes.c_void_p(16), ctypes.c_void_p(16), None, None)
+    assert rc == ep.EP_ERR_INVALID_ARG
+    # slot fill needs a multiple of 16 bytes per expert
+    lay_ok = ep._CLayout(12, 8, 16, 4, 5, ctypes.c_void_p(16))
+    rc = L.ep_slot_fill(ctypes.c_void_p(16), 24, ctypes.c_void_p(16), ctypes.byref(lay_ok),
+                        ctypes.c_void_p(16), None)
+    assert rc == ep.EP_ERR_INVALID_ARG
+
+
+def test_layout_init_rejects_bad_placement_on_host():
+    import moe_expert_load_layer_amd as ep
+    if not os.path.exists(ep.LIB_PATH):
+        pytest.skip("library not built")
+    L = ep.lib()
+    nc = (ctypes.c_int32 * 2)(1, 1)
+    ne = (ctypes.c_int32 * 2)(0, 0)          # expert 0 twice, expert 1 missing
+    sc = (ctypes.c_int32 * 2)(0, 1)
+    buf = (ctypes.c_int32 * 64)()
+    out = ep._CLayout()
+    rc = L.ep_layout_init(2, 2, ctypes.cast(nc, ctypes.c_void_p), ctypes.cast(ne, ctypes.c_void_p),
+                          ctypes.cast(sc, ctypes.c_void_p), ctypes.cast(buf, ctypes.c_void_p), 64,
+                          ctypes.byref(out))
+    assert rc == ep.EP_ERR_INVALID_ARG

@@ -1,0 +1,337 @@
+"""GPU parity: every step of the HIP path against the CPU oracle, bit-exact.
+
+Each kernel is first fed the oracle's own inputs (the planner gets the
+oracle's loads, the reroute the oracle's plan tables, the slot fill the
+oracle's phy2log), then the full chain runs on the GPU alone.  Tolerance is 0
+everywhere: the work is integer (plus one correctly rounded double division
+in the statistics) and a pure copy.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+ep = pytest.importorskip("moe_expert_load_layer_amd")
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def _small(name, tokens=37, layers=3, mbs=1):
+    wl = W.get(name)
+    return wl, wl.scaled(tokens_per_rank=min(tokens, wl.tokens_per_rank), layers=min(layers, wl.layers),
+                         microbatches=min(mbs, wl.microbatches))
+
+
+def _np(t):
+    return t.detach().cpu().numpy()
+
+
+def _stack_plans(plans):
+    return (np.stack([p.phy2log for p in plans]), np.stack([p.phy_quota for p in plans]),
+            np.stack([p.logcnt for p in plans]), np.stack([p.log2phy for p in plans]),
+            np.array([p.steps for p in plans]))
+
+
+def _assert_plan_equal(gpu_plan, ref_plans):
+    p2l, q, lc, l2p, steps = _stack_plans(ref_plans)
+    np.testing.assert_array_equal(_np(gpu_plan.phy2log), p2l)
+    np.testing.assert_array_equal(_np(gpu_plan.phy_quota), q)
+    np.testing.assert_array_equal(_np(gpu_plan.logcnt), lc)
+    np.testing.assert_array_equal(_np(gpu_plan.log2phy), l2p)
+    np.testing.assert_array_equal(_np(gpu_plan.steps), steps)
+
+
+# --------------------------------------------------------------------- A1
+@pytest.mark.parametrize("name", W.WORKLOAD_ORDER)
+def test_histogram_matches_oracle(dev, name):
+    wl, wls = _small(name)
+    ids = W.make_ids(wls)
+    print(f"[hist] {name} P={ids.shape[0]} N={ids.shape[1]}", flush=True)
+    lay = ep.Layout.from_workload(wl, device=dev)
+    load, ws, status = ep.ep_load_histogram(ids.to(dev), lay)
+    torch.cuda.synchronize()
+    for p in range(ids.shape[0]):
+        ref, bad = oracle.histogram(ids[p].numpy(), wl.num_experts)
+        np.testing.assert_array_equal(_np(load[p]), ref)
+        assert int(status[p]) == 0 and bad == 0
+
+
+@pytest.mark.parametrize("N", [0, 1, 3, 63, 64, 65, 2047, 2048, 2049, 6151, 20001])
+def test_histogram_sizes_padding_and_bad_ids(dev, N):
+    rng = np.random.default_rng(N)
+    E, P = 19, 3
+    ids = torch.from_numpy(rng.integers(0, E, size=(P, N)).astype(np.int32))
+    ids = W.inject_invalid(ids, E, 0.07, 0.03, seed=N) if N else ids
+    print(f"[hist-sizes] N={N}", flush=True)
+    lay = ep.Layout.create(E, [5, 5, 5, 4], list(range(E)), [1, 0, 2, 1], device=dev)
+    load, ws, status = ep.ep_load_histogram(ids.to(dev), lay)
+    torch.cuda.synchronize()
+    for p in range(P):
+        ref, bad = oracle.histogram(ids[p].numpy(), E)
+        np.testing.assert_array_equal(_np(load[p]), ref)
+        assert int(status[p]) == (ep.EP_STATUS_BAD_ID if bad else 0)
+
+
+# --------------------------------------------------------------------- A2
+@pytest.mark.parametrize("name", W.WORKLOAD_ORDER)
+def test_plan_matches_oracle(dev, name):
+    wl, wls = _small(name, tokens=200, layers=4, mbs=2)
+    lay_o = oracle.Layout.from_workload(wl)
+    ids = W.make_ids(wls).numpy()
+    loads = np.stack([oracle.histogram(ids[p], wl.num_experts)[0] for p in range(ids.shape[0])])
+    refs = [oracle.plan(l, lay_o) for l in loads]
+    print(f"[plan] {name} P={loads.shape[0]} steps={[r.steps for r in refs]}", flush=True)
+    lay = ep.Layout.from_workload(wl, device=dev)
+    status = torch.zeros(loads.shape[0], dtype=torch.int32, device=dev)
+    out = ep.ep_plan_quota(torch.from_numpy(loads).to(dev), lay, status=status)
+    torch.cuda.synchronize()
+    _assert_plan_equal(out, refs)
+    np.testing.assert_array_equal(_np(status), [ep.EP_STATUS_STEP_CAP if r.cap_hit else 0 for r in refs])
+
+
+def test_plan_hand_cases(dev):
+    cases = [
+        (3, [2, 1], [0, 1, 2], [0, 1], [8, 4, 2]),
+        (3, [1, 1, 1], [0, 1, 2], [1, 1, 0], [11, 0, 8]),
+        (4, [2, 1, 1], [0, 1, 2, 3], [0, 1, 1], [5, 5, 0, 0]),
+    ]
+    for E, nc, ne, sc, load in cases:
+        lay_o = oracle.Layout.of(E, len(nc), nc, ne, sc)
+        ref = oracle.plan(np.array(load), lay_o)
+        lay = ep.Layout.create(E, nc, ne, sc, device=dev)
+        out = ep.ep_plan_quota(torch.tensor([load], dtype=torch.int32, device=dev), lay)
+        torch.cuda.synchronize()
+        _assert_plan_equal(out, [ref])
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_plan_random_layouts(dev, seed):
+    rng = np.random.default_rng(1000 + seed)
+    for it in range(8):
+        E, R, nc, ne, sc = W.random_layout(rng, max_experts=70, max_ranks=40, max_spare_per_rank=3)
+        lay_o = oracle.Layout.of(E, R, nc, ne, sc)
+        if lay_o.max_replicas > 64:
+            continue
+        P = int(rng.integers(1, 5))
+        kind = it % 3
+        if kind == 0:
+            loads = rng.integers(0, 3000, size=(P, E))
+        elif kind == 1:
+            loads = (rng.pareto(0.8, size=(P, E)) * 50).astype(np.int64)
+        else:
+            loads = np.zeros((P, E), np.int64)
+            loads[:, rng.integers(0, E)] = rng.integers(1, 10**6)
+        loads = loads.astype(np.int32)
+        refs = [oracle.plan(l, lay_o) for l in loads]
+        lay = ep.Layout.create(E, nc, ne, sc, device=dev)
+        out = ep.ep_plan_quota(torch.from_numpy(loads).to(dev), lay)
+        torch.cuda.synchronize()
+        _assert_plan_equal(out, refs)
+
+
+def test_plan_max_replicas_64(dev):
+    # rho = 64: 64 ranks with 2 spares each; one expert carries most of the load
+    E, R = 64, 64
+    nc, ne, sc = [1] * R, list(range(E)), [2] * R
+    lay_o = oracle.Layout.of(E, R, nc, ne, sc)
+    assert lay_o.max_replicas == 64
+    rng = np.random.default_rng(9)
+    loads = rng.integers(0, 100, size=(3, E)).astype(np.int32)
+    loads[:, 5] = 10**6
+    loads[1, 7] = 5 * 10**5
+    refs = [oracle.plan(l, lay_o) for l in loads]
+    assert max(int(r.logcnt.max()) for r in refs) == 64
+    lay = ep.Layout.create(E, nc, ne, sc, device=dev)
+    out = ep.ep_plan_quota(torch.from_numpy(loads).to(dev), lay)
+    torch.cuda.synchronize()
+    _assert_plan_equal(out, refs)
+
+
+def test_plan_step_cap_flag(dev):
+    # rank 0 hosts all 6 hot experts; rank 1..3 have 3 spares each: the cap is
+    # 2*S+R = 22 moves; check the flag agrees with the oracle whatever it is
+    E, nc, ne, sc = 6, [6, 0, 0, 0], list(range(6)), [0, 3, 3, 3]
+    lay_o = oracle.Layout.of(E, 4, nc, ne, sc)
+    loads = np.array([[1000, 999, 998, 997, 996, 995]], np.int32)
+    ref = oracle.plan(loads[0], lay_o)
+    lay = ep.Layout.create(E, nc, ne, sc, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    out = ep.ep_plan_quota(torch.from_numpy(loads).to(dev), lay, status=status)
+    torch.cuda.synchronize()
+    _assert_plan_equal(out, [ref])
+    assert int(status[0]) == (ep.EP_STATUS_STEP_CAP if ref.cap_hit else 0)
+
+
+# --------------------------------------------------------------------- A3
+@pytest.mark.parametrize("name", W.WORKLOAD_ORDER)
+def test_reroute_with_oracle_plan(dev, name):
+    wl, wls = _small(name, tokens=45, layers=2, mbs=2)
+    lay_o = oracle.Layout.from_workload(wl)
+    ids = W.make_ids(wls)
+    print(f"[reroute] {name} P={ids.shape[0]} N={ids.shape[1]}", flush=True)
+    refs = [oracle.plan(oracle.histogram(ids[p].numpy(), wl.num_experts)[0], lay_o)
+            for p in range(ids.shape[0])]
+    p2l, q, lc, l2p, _ = _stack_plans(refs)
+    lay = ep.Layout.from_workload(wl, device=dev)
+    d_ids = ids.to(dev)
+    _, ws, _ = ep.ep_load_histogram(d_ids, lay)
+    phys = ep.ep_reroute(d_ids, lay, torch.from_numpy(q).to(dev), torch.from_numpy(l2p).to(dev),
+                         torch.from_numpy(lc).to(dev), ws)
+    torch.cuda.synchronize()
+    for p in range(ids.shape[0]):
+        ref, unplaced = oracle.reroute(ids[p].numpy(), wl.num_experts, q[p], l2p[p], lc[p])
+        assert unplaced == 0
+        np.testing.assert_array_equal(_np(phys[p]), ref)
+
+
+@pytest.mark.parametrize("N", [1, 5, 64, 2047, 2049, 9001, 33000])
+def test_reroute_padding_bad_and_short_quota(dev, N):
+    rng = np.random.default_rng(77 + N)
+    E, R = 21, 5
+    nc, ne, sc = [5, 4, 4, 4, 4], list(rng.permutation(E)), [2, 1, 0, 3, 1]
+    lay_o = oracle.Layout.of(E, R, nc, ne, sc)
+    P = 2
+    ids = torch.from_numpy(rng.choice(E, size=(P, N), p=rng.dirichlet(np.full(E, 0.2))).astype(np.int32))
+    ids = W.inject_invalid(ids, E, 0.05, 0.02, seed=N)
+    refs = [oracle.plan(oracle.histogram(ids[p].numpy(), E)[0], lay_o) for p in range(P)]
+    p2l, q, lc, l2p, _ = _stack_plans(refs)
+    q = q.copy()
+    # plan 1: shave one unit off a loaded instance so some pairs find no slot
+    nz = np.nonzero(q[1] > 0)[0]
+    if nz.size:
+        q[1, nz[0]] -= 1
+    lay = ep.Layout.create(E, nc, ne, sc, device=dev)
+    d_ids = ids.to(dev)
+    _, ws, _ = ep.ep_load_histogram(d_ids, lay)
+    phys = ep.ep_reroute(d_ids, lay, torch.from_numpy(q).to(dev), torch.from_numpy(l2p).to(dev),
+                         torch.from_numpy(lc).to(dev), ws)
+    torch.cuda.synchronize()
+    for p in range(P):
+        ref, _ = oracle.reroute(ids[p].numpy(), E, q[p], l2p[p], lc[p])
+        np.testing.assert_array_equal(_np(phys[p]), ref)
+
+
+def test_reroute_unaligned_rows(dev):
+    # N % 4 != 0: rows of later plans are not 16-byte aligned (scalar load path)
+    wl = W.get("qwen3_235b")
+    E = wl.num_experts
+    rng = np.random.default_rng(4)
+    N, P = 12345, 3
+    ids = torch.from_numpy(rng.integers(0, E, size=(P, N)).astype(np.int32))
+    lay_o = oracle.Layout.from_workload(wl)
+    lay = ep.Layout.from_workload(wl, device=dev)
+    d = ids.to(dev)
+    out = ep.run_path(d, lay)
+    torch.cuda.synchronize()
+    for p in range(P):
+        ld, _ = oracle.histogram(ids[p].numpy(), E)
+        pl = oracle.plan(ld, lay_o)
+        ph, _ = oracle.reroute(ids[p].numpy(), E, pl.phy_quota, pl.log2phy, pl.logcnt)
+        np.testing.assert_array_equal(_np(out["load"][p]), ld)
+        np.testing.assert_array_equal(_np(out["phys"][p]), ph)
+
+
+# --------------------------------------------------------------------- A4
+@pytest.mark.parametrize("name", ["tiny", "qwen3_235b", "deepseek_v3"])
+def test_slot_fill_with_oracle_plan(dev, name):
+    wl, wls = _small(name, tokens=64, layers=2)
+    lay_o = oracle.Layout.from_workload(wl)
+    ids = W.make_ids(wls).numpy()
+    elems = 64 * 32 if name == "tiny" else 4096 + 8      # small rows keep the host copy cheap
+    w = W.make_weights(wl, device=dev, elems_per_expert=elems)
+    w16 = _np(w.view(torch.int16))
+    lay = ep.Layout.from_workload(wl, device=dev)
+    for p in range(ids.shape[0]):
+        pl = oracle.plan(oracle.histogram(ids[p], wl.num_experts)[0], lay_o)
+        buf = torch.full((lay.num_spare, elems), 0x7FC1, dtype=torch.int16, device=dev).view(torch.bfloat16)
+        ep.ep_slot_fill(w, torch.from_numpy(pl.phy2log).to(dev), lay, buf)
+        torch.cuda.synchronize()
+        ref = np.full((lay_o.num_spare, elems), 0x7FC1, np.int16)
+        oracle.slot_fill(w16, pl.phy2log, lay_o, ref)
+        np.testing.assert_array_equal(_np(buf.view(torch.int16)), ref)
+
+
+# --------------------------------------------------------------------- A5
+@pytest.mark.parametrize("name", W.WORKLOAD_ORDER)
+def test_stats_with_oracle_inputs(dev, name):
+    wl, wls = _small(name, tokens=50, layers=3)
+    lay_o = oracle.Layout.from_workload(wl)
+    ids = W.make_ids(wls).numpy()
+    loads = np.stack([oracle.histogram(ids[p], wl.num_experts)[0] for p in range(ids.shape[0])])
+    plans = [oracle.plan(l, lay_o) for l in loads]
+    quotas = np.stack([p.phy_quota for p in plans])
+    lay = ep.Layout.from_workload(wl, device=dev)
+    st, imb, rl = ep.ep_balance_stats(torch.from_numpy(loads).to(dev), torch.from_numpy(quotas).to(dev), lay)
+    torch.cuda.synchronize()
+    for p in range(loads.shape[0]):
+        ref = oracle.stats(loads[p], quotas[p], lay_o)
+        np.testing.assert_array_equal(_np(st[p]), ref.as_row())
+        assert _np(imb[p]).tolist() == [ref.imbalance_before, ref.imbalance_after]
+        np.testing.assert_array_equal(_np(rl[p, 0]), ref.rank_before)
+        np.testing.assert_array_equal(_np(rl[p, 1]), ref.rank_after)
+
+
+def test_stats_zero_load(dev):
+    wl = W.get("tiny")
+    lay = ep.Layout.from_workload(wl, device=dev)
+    z = torch.zeros((1, 12), dtype=torch.int32, device=dev)
+    q = torch.zeros((1, 16), dtype=torch.int32, device=dev)
+    st, imb, _ = ep.ep_balance_stats(z, q, lay)
+    torch.cuda.synchronize()
+    assert _np(st[0]).tolist() == [0, 0, 0, 0] and _np(imb[0]).tolist() == [1.0, 1.0]
+
+
+# --------------------------------------------------------------------- chain
+@pytest.mark.parametrize("name", W.WORKLOAD_ORDER)
+def test_full_chain_small(dev, name):
+    wl, wls = _small(name, tokens=41, layers=3, mbs=2)
+    lay_o = oracle.Layout.from_workload(wl)
+    ids = W.make_ids(wls)
+    lay = ep.Layout.from_workload(wl, device=dev)
+    out = ep.run_path(ids.to(dev), lay)
+    torch.cuda.synchronize()
+    ref = oracle.run_path(ids.numpy(), lay_o)
+    np.testing.assert_array_equal(_np(out["load"]), ref["load"])
+    _assert_plan_equal(out["plan"], ref["plans"])
+    np.testing.assert_array_equal(_np(out["phys"]), ref["phys"])
+    np.testing.assert_array_equal(_np(out["stats"]), np.stack([s.as_row() for s in ref["stats"]]))
+
+
+def test_empty_and_all_padding(dev):
+    wl = W.get("tiny")
+    lay = ep.Layout.from_workload(wl, device=dev)
+    lay_o = oracle.Layout.from_workload(wl)
+    for N in (0, 300):
+        ids = torch.full((2, N), -1, dtype=torch.int32)
+        out = ep.run_path(ids.to(dev), lay)
+        torch.cuda.synchronize()
+        assert int(out["load"].abs().sum()) == 0
+        ref = oracle.plan(np.zeros(12, np.int32), lay_o)
+        _assert_plan_equal(out["plan"], [ref, ref])
+        if N:
+            assert bool((out["phys"] == -1).all())
+
+
+def test_deterministic_and_stream_independent(dev):
+    wl, wls = _small("stress", tokens=300, layers=2, mbs=1)
+    lay = ep.Layout.from_workload(wl, device=dev)
+    ids = W.make_ids(wls, device=dev)
+    a = ep.run_path(ids, lay)
+    s2 = torch.cuda.Stream()
+    with torch.cuda.stream(s2):
+        b = ep.run_path(ids, lay)
+    s2.synchronize()
+    torch.cuda.synchronize()
+    for k in ("load", "phys", "stats"):
+        assert torch.equal(a[k], b[k]), k
+    assert torch.equal(a["plan"].log2phy, b["plan"].log2phy)
+    assert torch.equal(a["plan"].phy_quota, b["plan"].phy_quota)
