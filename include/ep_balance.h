@@ -79,6 +79,8 @@ typedef struct ep_layout {
     int32_t num_phys;     /* Phi = E + S physical slots                           */
     int32_t num_spare;    /* S: spare slots over all ranks                        */
     int32_t max_replicas; /* rho = min(R, 1 + S): row width of log2phy            */
+    int32_t max_rank_natives; /* most native experts on one rank                  */
+    int32_t max_rank_spares;  /* most spare slots on one rank                     */
     const int32_t *tables;/* device, packed tables (see ep_layout_init)           */
 } ep_layout_t;
 

@@ -36,6 +36,8 @@ class _CLayout(ctypes.Structure):
         ("num_phys", ctypes.c_int32),
         ("num_spare", ctypes.c_int32),
         ("max_replicas", ctypes.c_int32),
+        ("max_rank_natives", ctypes.c_int32),
+        ("max_rank_spares", ctypes.c_int32),
         ("tables", ctypes.c_void_p),
     ]
 

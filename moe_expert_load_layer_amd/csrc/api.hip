@@ -27,6 +27,8 @@ bool layout_ok(const ep_layout_t *L) {
     if (L->num_spare < 0 || L->num_phys != L->num_experts + L->num_spare) return false;
     const int32_t rho = L->num_ranks < 1 + L->num_spare ? L->num_ranks : 1 + L->num_spare;
     if (L->max_replicas != rho) return false;
+    if (L->max_rank_natives < 0 || L->max_rank_natives > L->num_experts) return false;
+    if (L->max_rank_spares < 0 || L->max_rank_spares > L->num_spare) return false;
     return aligned(L->tables, 4);
 }
 
@@ -53,10 +55,13 @@ int ep_layout_init(int32_t E, int32_t R, const int32_t *native_count, const int3
     if (E < 1 || E > EP_MAX_EXPERTS || R < 1 || R > EP_MAX_RANKS || !aligned(device_tables, 4))
         return EP_ERR_INVALID_ARG;
     int64_t nat_total = 0, S = 0;
+    int32_t max_nat = 0, max_sp = 0;
     for (int r = 0; r < R; r++) {
         if (native_count[r] < 0 || spare_count[r] < 0) return EP_ERR_INVALID_ARG;
         nat_total += native_count[r];
         S += spare_count[r];
+        max_nat = native_count[r] > max_nat ? native_count[r] : max_nat;
+        max_sp = spare_count[r] > max_sp ? spare_count[r] : max_sp;
     }
     if (nat_total != E || S > (int64_t)EP_MAX_EXPERTS * 64) return EP_ERR_INVALID_ARG;
     const int Phi = E + (int)S;
@@ -108,6 +113,8 @@ int ep_layout_init(int32_t E, int32_t R, const int32_t *native_count, const int3
     out->num_phys = Phi;
     out->num_spare = (int32_t)S;
     out->max_replicas = R < 1 + (int32_t)S ? R : 1 + (int32_t)S;
+    out->max_rank_natives = max_nat;
+    out->max_rank_spares = max_sp;
     out->tables = device_tables;
     return EP_OK;
 }
@@ -136,9 +143,10 @@ int ep_plan_quota(const int32_t *load, int32_t P, const ep_layout_t *layout, int
     if (!layout_ok(layout) || !load || !phy2log || !phy_quota || !logcnt || !log2phy)
         return EP_ERR_INVALID_ARG;
     if (P < 1 || P > kMaxPlans || layout->max_replicas > 64) return EP_ERR_INVALID_ARG;
-    if (plan_lds_bytes(*layout) > kMaxLds) return EP_ERR_INVALID_ARG;
+    const int spr = plan_lanes_spr(*layout, layout->max_rank_spares, layout->max_rank_natives);
+    if (spr == 0 && plan_lds_bytes(*layout) > kMaxLds) return EP_ERR_INVALID_ARG;
     return hip_rc(launch_plan(load, P, *layout, phy2log, phy_quota, logcnt, log2phy, steps, status,
-                              as_stream(stream)));
+                              as_stream(stream), spr));
 }
 
 int ep_reroute(const int32_t *topk_ids, int64_t N, int32_t P, const ep_layout_t *layout,

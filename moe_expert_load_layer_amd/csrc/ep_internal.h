@@ -5,7 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/ep_balance.h"
+#include "ep_balance.h"
 
 namespace ep {
 
@@ -51,22 +51,36 @@ inline Tables tables_of(const ep_layout_t &L) {
 // waves in a launch, keeps the count table under 1/4 byte per pair
 // (>= 16 (E+1) pairs), and is a power of two between 2048 and 32768.
 // ---------------------------------------------------------------------------
+#ifndef EP_SUB_TARGET_WAVES
+#define EP_SUB_TARGET_WAVES 8192
+#endif
+#ifndef EP_SUB_MAX
+#define EP_SUB_MAX 8192
+#endif
+#ifndef EP_SUB_MIN
+#define EP_SUB_MIN 2048
+#endif
 inline int64_t sub_pairs(int64_t N, int32_t P, int32_t E) {
-    int64_t want = (N * (int64_t)P + 8191) / 8192;
+    const int64_t tw = EP_SUB_TARGET_WAVES;
+    int64_t want = (N * (int64_t)P + tw - 1) / tw;
     int64_t lo = 16 * (int64_t)(E + 1);
-    if (lo < 2048) lo = 2048;
+    if (lo < EP_SUB_MIN) lo = EP_SUB_MIN;
     if (want < lo) want = lo;
-    int64_t sub = 2048;
-    while (sub < want && sub < 32768) sub <<= 1;
+    int64_t sub = EP_SUB_MIN;
+    while (sub < want && sub < EP_SUB_MAX) sub <<= 1;
     while (sub < lo) sub <<= 1;
+#ifdef EP_SUB_FIXED
+    sub = EP_SUB_FIXED;
+#endif
     return sub;
 }
 
 inline int64_t num_sub(int64_t N, int64_t sub) { return N <= 0 ? 0 : (N + sub - 1) / sub; }
 
+// per plan: one count row per sub-block plus one row of per-expert totals
 inline size_t ws_bytes(int64_t N, int32_t P, int32_t E) {
     const int64_t sub = sub_pairs(N, P, E);
-    return (size_t)P * (size_t)num_sub(N, sub) * (size_t)(E + 1) * sizeof(int32_t);
+    return (size_t)P * (size_t)(num_sub(N, sub) + 1) * (size_t)(E + 1) * sizeof(int32_t);
 }
 
 // ---------------------------------------------------------------------------
@@ -137,6 +151,29 @@ __device__ __forceinline__ int64_t readlane_i64(int64_t v, int lane) {
     return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
+// Row-level (16-lane) DPP reductions finished with four readlanes: no LDS
+// traffic.  dpp controls: quad_perm [1,0,3,2] = 0xB1, [2,3,0,1] = 0x4E,
+// row_half_mirror = 0x141, row_mirror = 0x140.
+__device__ __forceinline__ int wave_max_i32(int v) {
+    v = max(v, __builtin_amdgcn_update_dpp(v, v, 0xB1, 0xF, 0xF, false));
+    v = max(v, __builtin_amdgcn_update_dpp(v, v, 0x4E, 0xF, 0xF, false));
+    v = max(v, __builtin_amdgcn_update_dpp(v, v, 0x141, 0xF, 0xF, false));
+    v = max(v, __builtin_amdgcn_update_dpp(v, v, 0x140, 0xF, 0xF, false));
+    const int a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+    const int c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+    return max(max(a, b), max(c, d));
+}
+
+__device__ __forceinline__ int wave_min_i32(int v) {
+    v = min(v, __builtin_amdgcn_update_dpp(v, v, 0xB1, 0xF, 0xF, false));
+    v = min(v, __builtin_amdgcn_update_dpp(v, v, 0x4E, 0xF, 0xF, false));
+    v = min(v, __builtin_amdgcn_update_dpp(v, v, 0x141, 0xF, 0xF, false));
+    v = min(v, __builtin_amdgcn_update_dpp(v, v, 0x140, 0xF, 0xF, false));
+    const int a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+    const int c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+    return min(min(a, b), min(c, d));
+}
+
 // orders LDS accesses of the lanes of one wave (no workgroup barrier)
 __device__ __forceinline__ void wave_lds_fence() {
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
@@ -149,10 +186,13 @@ __device__ __forceinline__ void wave_lds_fence() {
 hipError_t launch_histogram(const int32_t *ids, int64_t N, int32_t P, int32_t E, int64_t sub,
                             int64_t nsb, int32_t *ws, int32_t *load, uint32_t *status,
                             hipStream_t s);
+// spr > 0 selects the rank-per-lane planner with that many spare registers per
+// lane (see plan_lanes_spr); spr == 0 selects the generic planner
 hipError_t launch_plan(const int32_t *load, int32_t P, const ep_layout_t &L, int32_t *phy2log,
                        int32_t *phy_quota, int32_t *logcnt, int32_t *log2phy, int32_t *steps,
-                       uint32_t *status, hipStream_t s);
+                       uint32_t *status, hipStream_t s, int spr);
 size_t plan_lds_bytes(const ep_layout_t &L);
+int plan_lanes_spr(const ep_layout_t &L, int max_spare_per_rank, int max_native_per_rank);
 hipError_t launch_reroute(const int32_t *ids, int64_t N, int32_t P, const ep_layout_t &L,
                           int64_t sub, int64_t nsb, const int32_t *ws, const int32_t *phy_quota,
                           const int32_t *log2phy, const int32_t *logcnt, int32_t *out,

@@ -16,7 +16,13 @@
 namespace ep {
 namespace {
 
-constexpr int kHistWaves = 4;
+#ifndef EP_HIST_WAVES
+#define EP_HIST_WAVES 4
+#endif
+#ifndef EP_HIST_UNROLL
+#define EP_HIST_UNROLL 4
+#endif
+constexpr int kHistWaves = EP_HIST_WAVES;
 
 __global__ __launch_bounds__(kHistWaves * kWave) void hist_kernel(
     const int32_t *__restrict__ ids, int64_t N, int32_t E, int64_t sub, int64_t nsb,
@@ -52,7 +58,7 @@ __global__ __launch_bounds__(kHistWaves * kWave) void hist_kernel(
     if (((uintptr_t)(src + begin) & 15) == 0) {
         const int64_t nvec = (end - begin) / 4;
         const i32x4 *v4 = reinterpret_cast<const i32x4 *>(src + begin);
-        constexpr int U = 4;
+        constexpr int U = EP_HIST_UNROLL;
         int64_t k = lane;
         for (; k + (U - 1) * kWave < nvec; k += U * kWave) {
             i32x4 x[U];
@@ -73,12 +79,16 @@ __global__ __launch_bounds__(kHistWaves * kWave) void hist_kernel(
     if (nbad) atomicAdd(&h[E], nbad);
     wave_lds_fence();
 
-    int32_t *row = ws + ((int64_t)p * nsb + sb) * E1;
+    int32_t *row = ws + ((int64_t)p * (nsb + 1) + sb) * E1;
     for (int e = lane; e < E1; e += kWave) row[e] = h[e];
 }
 
-constexpr int kScanWaves = 4;
+constexpr int kScanWaves = 16;
+constexpr int kScanUnroll = 8;
 
+// Workspace rows per plan: nsb sub-block rows, then one row of per-expert
+// totals (the plan's load), which lets the reroute skip ranking pairs of an
+// expert whose single instance takes all of its pairs.
 __global__ __launch_bounds__(kScanWaves * kWave) void scan_kernel(
     int32_t *__restrict__ ws, int64_t nsb, int32_t E, int32_t *__restrict__ load,
     uint32_t *__restrict__ status) {
@@ -88,14 +98,24 @@ __global__ __launch_bounds__(kScanWaves * kWave) void scan_kernel(
     const int E1 = E + 1;
     const int p = blockIdx.y;
     const int col = blockIdx.x * kWave + lane;
-    int32_t *base = ws + (int64_t)p * nsb * E1;
+    int32_t *base = ws + (int64_t)p * (nsb + 1) * E1;
     const int64_t seg = (nsb + kScanWaves - 1) / kScanWaves;
-    const int64_t b0 = wave * seg;
+    const int64_t b0 = wave * seg < nsb ? wave * seg : nsb;
     const int64_t b1 = (b0 + seg < nsb) ? b0 + seg : nsb;
+    const bool on = col < E1;
 
     int32_t sum = 0;
-    if (col < E1)
-        for (int64_t b = b0; b < b1; b++) sum += base[b * E1 + col];
+    if (on) {
+        int64_t b = b0;
+        for (; b + kScanUnroll <= b1; b += kScanUnroll) {
+            int32_t c[kScanUnroll];
+#pragma unroll
+            for (int u = 0; u < kScanUnroll; u++) c[u] = base[(b + u) * E1 + col];
+#pragma unroll
+            for (int u = 0; u < kScanUnroll; u++) sum += c[u];
+        }
+        for (; b < b1; b++) sum += base[b * E1 + col];
+    }
     part[wave][lane] = sum;
     __syncthreads();
     int32_t run = 0, total = 0;
@@ -103,13 +123,25 @@ __global__ __launch_bounds__(kScanWaves * kWave) void scan_kernel(
         if (w < wave) run += part[w][lane];
         total += part[w][lane];
     }
-    if (col < E1) {
-        for (int64_t b = b0; b < b1; b++) {
+    if (on) {
+        int64_t b = b0;
+        for (; b + kScanUnroll <= b1; b += kScanUnroll) {
+            int32_t c[kScanUnroll];
+#pragma unroll
+            for (int u = 0; u < kScanUnroll; u++) c[u] = base[(b + u) * E1 + col];
+#pragma unroll
+            for (int u = 0; u < kScanUnroll; u++) {
+                base[(b + u) * E1 + col] = run;
+                run += c[u];
+            }
+        }
+        for (; b < b1; b++) {
             const int32_t c = base[b * E1 + col];
             base[b * E1 + col] = run;
             run += c;
         }
         if (wave == 0) {
+            base[nsb * E1 + col] = total;
             if (col < E) load[(int64_t)p * E + col] = total;
             else status[p] = total > 0 ? (uint32_t)EP_STATUS_BAD_ID : 0u;
         }

@@ -31,7 +31,7 @@ struct PlanArgs {
 
 __device__ __forceinline__ uint32_t inv(uint32_t x) { return 0xffffffffu - x; }
 
-__global__ __launch_bounds__(kWave) void plan_kernel(const int32_t *__restrict__ load, PlanArgs a,
+__global__ __launch_bounds__(kWave) void plan_kernel_generic(const int32_t *__restrict__ load, PlanArgs a,
                                                      int32_t *__restrict__ phy2log,
                                                      int32_t *__restrict__ phy_quota,
                                                      int32_t *__restrict__ logcnt,
@@ -256,6 +256,223 @@ __global__ __launch_bounds__(kWave) void plan_kernel(const int32_t *__restrict__
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// Rank-per-lane planner (R <= 64, at most SPR spare slots per rank).
+//
+// Lane r owns rank r: its load, its free spare count and the owner and quota
+// of each of its spare slots live in registers.  The instances of an expert
+// are then found lane-locally (native rank, or a spare slot of the lane that
+// holds the expert), the water-fill runs over the lanes that host the expert,
+// and a commit only touches those lanes' registers plus the native quota in
+// LDS.  Cross-lane steps are DPP reductions, ballots and readlanes.
+// ---------------------------------------------------------------------------
+struct ExpertInfo {
+    int32_t nq;     // quota of the native instance
+    int32_t icnt;   // instances (native + replicas)
+    int32_t load;   // the expert's load
+    int32_t nrank;  // rank of the native instance
+};
+
+template <int SPR>
+__global__ __launch_bounds__(kWave) void plan_kernel_lanes(const int32_t *__restrict__ load, PlanArgs a,
+                                                           int32_t *__restrict__ phy2log,
+                                                           int32_t *__restrict__ phy_quota,
+                                                           int32_t *__restrict__ logcnt,
+                                                           int32_t *__restrict__ log2phy,
+                                                           int32_t *__restrict__ steps_out,
+                                                           uint32_t *__restrict__ status) {
+    const int E = a.E, R = a.R, Phi = a.Phi, S = a.S, rho = a.rho;
+    extern __shared__ __align__(16) unsigned char sh_raw[];
+    ExpertInfo *info = reinterpret_cast<ExpertInfo *>(sh_raw);           // [E]
+    uint64_t *emask = reinterpret_cast<uint64_t *>(info + E);             // [E]
+    int32_t *shome = reinterpret_cast<int32_t *>(emask + E);              // [Phi]
+
+    const int p = blockIdx.x;
+    const int lane = threadIdx.x;
+    const int32_t *lp = load + (int64_t)p * E;
+
+    for (int s = lane; s < Phi; s += kWave) shome[s] = a.T.slot_home[s];
+    for (int e = lane; e < E; e += kWave) {
+        const int l = lp[e];
+        info[e] = ExpertInfo{l, 1, l, a.T.slot_rank[a.T.home_slot[e]]};
+        emask[e] = 0;
+    }
+    // rank-lane registers
+    const bool is_rank = lane < R;
+    const int f0 = is_rank ? a.T.rank_first[lane] : 0;
+    const int nat = is_rank ? a.T.rank_nat[lane] : 0;
+    const int spc = is_rank ? a.T.rank_first[lane + 1] - f0 - nat : 0;
+    int freec = spc;
+    int sp_owner[SPR], sp_q[SPR];
+#pragma unroll
+    for (int j = 0; j < SPR; j++) { sp_owner[j] = -1; sp_q[j] = 0; }
+    __syncthreads();
+    int rl = 0;
+    for (int i = 0; i < nat; i++) rl += info[shome[f0 + i]].load;
+    if (!is_rank) rl = 0;
+
+    const int cap = 2 * S + R;
+    int steps = 0, cap_hit = 0;
+    for (;;) {
+        if (steps == cap) { cap_hit = 1; break; }
+        // hottest rank (lowest index on ties)
+        const int vmax = wave_max_i32(is_rank ? rl : -1);
+        const int h = __ffsll((long long)__ballot(is_rank && rl == vmax)) - 1;
+        const int Lh = vmax;
+
+        // candidates: h's natives in lanes [0, nat_h), h's spare slots after them
+        const int nat_h = __builtin_amdgcn_readlane(nat, h);
+        const int f0_h = __builtin_amdgcn_readlane(f0, h);
+        int ce = -1, cq = 0;
+        if (lane < nat_h) ce = shome[f0_h + lane];
+#pragma unroll
+        for (int j = 0; j < SPR; j++) {
+            const int oe = __builtin_amdgcn_readlane(sp_owner[j], h);
+            const int oq = __builtin_amdgcn_readlane(sp_q[j], h);
+            if (lane == nat_h + j) { ce = oe; cq = oq; }
+        }
+        ExpertInfo ci{0, 0, 0, 0};
+        if (ce >= 0) ci = info[ce];
+        if (lane < nat_h) cq = ci.nq;
+        const bool valid = ce >= 0 && cq > 0;
+        const uint64_t key = valid ? (((uint64_t)(uint32_t)cq << 32) | inv((uint32_t)ce)) : 0;
+        // order of the candidates: count the larger keys
+        const uint64_t vm = __ballot(valid);
+        int crank = 0;
+        for (uint64_t mm = vm; mm; mm &= mm - 1) {
+            const int j = __ffsll((long long)mm) - 1;
+            const uint64_t kj = (uint64_t)readlane_i64((int64_t)key, j);
+            crank += kj > key ? 1 : 0;
+        }
+        const int nc = __popcll(vm);
+
+        bool committed = false;
+        for (int pass = 0; pass < 2 && !committed; pass++) {
+            for (int c = 0; c < nc && !committed; c++) {
+                const int cl = __ffsll((long long)__ballot(valid && crank == c)) - 1;
+                const int e = __builtin_amdgcn_readlane(ce, cl);
+                if (pass == 0 && __builtin_amdgcn_readlane(ci.icnt, cl) < 2) continue;
+                const int T = __builtin_amdgcn_readlane(ci.load, cl);
+                const int nr = __builtin_amdgcn_readlane(ci.nrank, cl);
+                const int nqe = __builtin_amdgcn_readlane(ci.nq, cl);
+                const bool replicate = pass == 1;
+
+                // instances of e on this lane's rank
+                const bool nat_here = lane == nr;
+                int jr = -1;
+#pragma unroll
+                for (int j = 0; j < SPR; j++)
+                    if (j < spc && sp_owner[j] == e) jr = j;
+                int q = 0;
+#pragma unroll
+                for (int j = 0; j < SPR; j++)
+                    if (j == jr) q = sp_q[j];
+                if (nat_here) q = nqe;
+                const bool inst = nat_here || jr >= 0;
+                const int b = rl - q;
+                bool isnew = false;
+                if (replicate) {
+                    const bool elig = is_rank && freec > 0 && !inst;
+                    const int vmin = wave_min_i32(elig ? rl : 0x7fffffff);
+                    const uint64_t em = __ballot(elig && rl == vmin);
+                    if (em == 0) continue;
+                    isnew = lane == __ffsll((long long)em) - 1;
+                }
+                const bool act = inst || isnew;
+                // sorted position by (background, rank) and inclusive prefix sum
+                int pos = 0;
+                int64_t Sinc = T;
+                for (uint64_t mm = __ballot(act); mm; mm &= mm - 1) {
+                    const int j = __ffsll((long long)mm) - 1;
+                    const int bj = __builtin_amdgcn_readlane(b, j);
+                    const bool less = bj < b || (bj == b && j < lane);
+                    pos += less ? 1 : 0;
+                    if (less || j == lane) Sinc += bj;
+                }
+                // the filled instances form a prefix of the sorted order, so
+                // m* = number of instances with m*b_(m) < S_m
+                const int mstar = __popcll(__ballot(act && (int64_t)(pos + 1) * b < Sinc));
+                int qn = 0;
+                if (mstar > 0) {
+                    const int ls = __ffsll((long long)__ballot(act && pos == mstar - 1)) - 1;
+                    const uint32_t Ss = (uint32_t)readlane_i64(Sinc, ls);
+                    const uint32_t base = Ss / (uint32_t)mstar;
+                    const uint32_t rem = Ss - (uint32_t)mstar * base;
+                    if (act && pos < mstar) qn = (int)base - b + ((uint32_t)pos < rem ? 1 : 0);
+                }
+                const int newLh = __builtin_amdgcn_readlane(act ? b + qn : rl, h);
+                if (newLh >= Lh) continue;
+                // commit (lane-local, plus the native quota and count in LDS)
+                if (act) rl = b + qn;
+                if (nat_here) info[e].nq = qn;
+#pragma unroll
+                for (int j = 0; j < SPR; j++)
+                    if (j == jr) sp_q[j] = qn;
+                if (isnew) {
+                    const int jn = spc - freec;
+#pragma unroll
+                    for (int j = 0; j < SPR; j++)
+                        if (j == jn) { sp_owner[j] = e; sp_q[j] = qn; }
+                    freec -= 1;
+                    info[e].icnt += 1;
+                }
+                wave_lds_fence();
+                committed = true;
+            }
+        }
+        if (!committed) break;
+        steps++;
+    }
+
+    // replicas left without load are freed; record each live replica's rank
+#pragma unroll
+    for (int j = 0; j < SPR; j++) {
+        if (j < spc && sp_owner[j] >= 0 && sp_q[j] == 0) sp_owner[j] = -1;
+        if (j < spc && sp_owner[j] >= 0)
+            atomicOr(reinterpret_cast<unsigned long long *>(&emask[sp_owner[j]]), 1ull << lane);
+    }
+    __syncthreads();
+
+    int32_t *o_p2l = phy2log + (int64_t)p * Phi;
+    int32_t *o_q = phy_quota + (int64_t)p * Phi;
+    int32_t *o_l2p = log2phy + (int64_t)p * E * rho;
+    // spare slots: owner, quota and place in the owner's log2phy row
+    // (instances are one per rank, so ascending slot = ascending rank)
+#pragma unroll
+    for (int j = 0; j < SPR; j++) {
+        if (j < spc) {
+            const int s = f0 + nat + j;
+            const int e = sp_owner[j];
+            o_p2l[s] = e;
+            o_q[s] = e >= 0 ? sp_q[j] : 0;
+            if (e >= 0) {
+                const uint64_t below = emask[e] & ((1ull << lane) - 1);
+                const int pos = __popcll(below) + (info[e].nrank < lane ? 1 : 0);
+                o_l2p[(int64_t)e * rho + pos] = s;
+            }
+        }
+    }
+    // natives, counts, native position and padding
+    for (int e = lane; e < E; e += kWave) {
+        const ExpertInfo in = info[e];
+        const uint64_t m = emask[e];
+        const int hs = a.T.home_slot[e];
+        o_p2l[hs] = e;
+        o_q[hs] = in.nq;
+        const int cnt = 1 + __popcll(m);
+        logcnt[(int64_t)p * E + e] = cnt;
+        const int npos = __popcll(m & ((1ull << in.nrank) - 1));
+        int32_t *row = o_l2p + (int64_t)e * rho;
+        row[npos] = hs;
+        for (int t = cnt; t < rho; t++) row[t] = -1;
+    }
+    if (lane == 0) {
+        if (steps_out) steps_out[p] = steps;
+        if (status && cap_hit) status[p] |= (uint32_t)EP_STATUS_STEP_CAP;
+    }
+}
+
 }  // namespace
 
 size_t plan_lds_bytes(const ep_layout_t &L) {
@@ -263,12 +480,36 @@ size_t plan_lds_bytes(const ep_layout_t &L) {
     return 8 * E + 8 * kWave + 4 * (5 * R + 1 + 3 * Phi + 5 * E + S + kWave);
 }
 
+static size_t lanes_lds_bytes(const ep_layout_t &L) {
+    return (size_t)L.num_experts * (sizeof(ExpertInfo) + 8) + (size_t)L.num_phys * 4;
+}
+
+int plan_lanes_spr(const ep_layout_t &L, int max_spare_per_rank, int max_native_per_rank) {
+    if (L.num_ranks > kWave) return 0;
+    int spr = 1;
+    while (spr < max_spare_per_rank) spr <<= 1;
+    if (spr > 16 || max_native_per_rank + spr > kWave) return 0;
+    if (lanes_lds_bytes(L) > 65536) return 0;
+    return spr;
+}
+
 hipError_t launch_plan(const int32_t *load, int32_t P, const ep_layout_t &L, int32_t *phy2log,
                        int32_t *phy_quota, int32_t *logcnt, int32_t *log2phy, int32_t *steps,
-                       uint32_t *status, hipStream_t s) {
+                       uint32_t *status, hipStream_t s, int spr) {
     PlanArgs a{L.num_experts, L.num_ranks, L.num_phys, L.num_spare, L.max_replicas, tables_of(L)};
-    hipLaunchKernelGGL(plan_kernel, dim3((unsigned)P), dim3(kWave), plan_lds_bytes(L), s, load, a,
-                       phy2log, phy_quota, logcnt, log2phy, steps, status);
+    const dim3 g((unsigned)P), b(kWave);
+    const size_t lds = lanes_lds_bytes(L);
+    switch (spr) {
+        case 1: hipLaunchKernelGGL(plan_kernel_lanes<1>, g, b, lds, s, load, a, phy2log, phy_quota, logcnt, log2phy, steps, status); break;
+        case 2: hipLaunchKernelGGL(plan_kernel_lanes<2>, g, b, lds, s, load, a, phy2log, phy_quota, logcnt, log2phy, steps, status); break;
+        case 4: hipLaunchKernelGGL(plan_kernel_lanes<4>, g, b, lds, s, load, a, phy2log, phy_quota, logcnt, log2phy, steps, status); break;
+        case 8: hipLaunchKernelGGL(plan_kernel_lanes<8>, g, b, lds, s, load, a, phy2log, phy_quota, logcnt, log2phy, steps, status); break;
+        case 16: hipLaunchKernelGGL(plan_kernel_lanes<16>, g, b, lds, s, load, a, phy2log, phy_quota, logcnt, log2phy, steps, status); break;
+        default:
+            hipLaunchKernelGGL(plan_kernel_generic, g, b, plan_lds_bytes(L), s, load, a, phy2log,
+                               phy_quota, logcnt, log2phy, steps, status);
+            break;
+    }
     return hipGetLastError();
 }
 

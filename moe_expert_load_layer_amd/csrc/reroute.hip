@@ -3,18 +3,143 @@
 // EPLB tutorial: the physical replica is looked up from the logical top-k ID).
 //
 // One wave per sub-block, the same sub-blocks the histogram counted.  The
-// scanned workspace row gives, for every expert, how many of its pairs come
-// before the sub-block.  Inside the sub-block the wave walks 64 pairs at a time
-// in flat order; the stable rank of a pair among equal IDs of the group comes
-// from an LDS bit mask per expert (each lane ORs its bit, then counts the bits
-// below it), so no atomic order is involved.  The group leader of each expert
-// advances that expert's running count.  The rank j then selects the instance
-// whose cumulative quota range holds j (binary search over the expert's
-// instances, which the block lays out in LDS from log2phy and phy_quota).
+// scanned workspace rows give, for every expert e, the rank range
+// [run_e, next_e) its pairs of this sub-block occupy in flat (source rank,
+// token, k) order.  If no quota boundary of e falls inside that range, every
+// one of those pairs goes to the same instance (or to -1 beyond the last
+// quota), so the wave first writes a per-expert code table in LDS: a physical
+// slot, -1, or "split".  A plan has at most one boundary per replica, so split
+// (sub-block, expert) cells are rare; only their pairs are ranked one by one:
+// per split expert, a wave prefix sum over lanes of the counts in flat order.
+// Everything else is one LDS read per pair, and the IDs stream in and the
+// physical IDs stream out as 16-byte accesses.
 #include "ep_internal.h"
 
 namespace ep {
 namespace {
+
+#ifndef EP_RR_UNROLL
+#define EP_RR_UNROLL 4
+#endif
+#ifndef EP_RR_MAX_WAVES
+#define EP_RR_MAX_WAVES 4
+#endif
+
+constexpr int32_t kSplit = (int32_t)0x80000000;
+
+// first instance t in [0, n) of the list at `inst` whose cumulative end exceeds j
+__device__ __forceinline__ int first_above(const int2 *inst, int n, int32_t j) {
+    int lo = 0, hi = n;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (j < inst[mid].x) hi = mid; else lo = mid + 1;
+    }
+    return lo;
+}
+
+// Split experts of a sub-block.  The first 64 live one per lane in registers
+// (rank counter, current instance, its cumulative end and slot); their pairs
+// carry the code kSplit | index.  Any further split expert (code kSplitLds)
+// keeps its rank counter in LDS and is looked up by binary search.
+struct SplitRegs {
+    int32_t run;   // rank of the expert's next pair
+    int32_t f, n;  // its instance list in the block table
+    int32_t t;     // instance holding `run`
+    int32_t end;   // cumulative end of instance t (INT32_MAX past the last)
+    int32_t phys;  // slot of instance t (-1 past the last)
+};
+
+constexpr int32_t kSplitLds = (int32_t)(0x80000000u | 127u);
+
+__device__ __forceinline__ bool is_split(int32_t c) { return c < -1; }
+
+__device__ __forceinline__ void seek(SplitRegs &sr, const int2 *inst) {
+    sr.t = first_above(inst + sr.f, sr.n, sr.run);
+    sr.end = sr.t < sr.n ? inst[sr.f + sr.t].x : 0x7fffffff;
+    sr.phys = sr.t < sr.n ? inst[sr.f + sr.t].y : -1;
+}
+
+// Rank the pairs of split experts in one group and replace their codes by the
+// instance slot.  K consecutive pairs per lane; flat order is (lane, k), so
+// the rank of (l, k) among pairs of one expert in the group is the number of
+// its bits below lane l in the K column ballots plus its pairs in columns
+// k' < k of lane l.  Loops once per distinct split expert present.
+template <int K>
+__device__ __forceinline__ void resolve_split(const int32_t (&x)[K], int32_t (&c)[K],
+                                              SplitRegs &sr, const int32_t *rfirst,
+                                              const int32_t *rcnt, const int2 *inst,
+                                              int32_t *srun) {
+    const uint64_t lt = lanemask_lt();
+    const int lane = lane_id();
+    uint32_t pend = 0;
+#pragma unroll
+    for (int k = 0; k < K; k++) pend |= (is_split(c[k]) ? 1u : 0u) << k;
+    for (;;) {
+        const uint64_t any = __ballot(pend != 0);
+        if (any == 0) break;
+        const int leader = __ffsll((long long)any) - 1;
+        int32_t mc = 0, mx = 0;
+#pragma unroll
+        for (int k = K - 1; k >= 0; k--)
+            if (pend & (1u << k)) { mc = c[k]; mx = x[k]; }
+        const int32_t cc = __builtin_amdgcn_readlane(mc, leader);
+        const int32_t y = __builtin_amdgcn_readlane(mx, leader);
+        uint32_t hit = 0;
+        int below = 0, tot = 0;
+#pragma unroll
+        for (int k = 0; k < K; k++) {
+            const bool h = ((pend >> k) & 1u) && x[k] == y;
+            hit |= (h ? 1u : 0u) << k;
+            const uint64_t m = __ballot(h);
+            below += __popcll(m & lt);
+            tot += __popcll(m);
+        }
+        if (cc != kSplitLds) {
+            const int idx = cc & 0x7f;
+            const int32_t run = __builtin_amdgcn_readlane(sr.run, idx);
+            const int32_t rend = __builtin_amdgcn_readlane(sr.end, idx);
+            if (run + tot <= rend) {
+                // the whole group sits in one instance
+                const int32_t ph = __builtin_amdgcn_readlane(sr.phys, idx);
+#pragma unroll
+                for (int k = 0; k < K; k++)
+                    if ((hit >> k) & 1u) c[k] = ph;
+            } else {
+                const int f = __builtin_amdgcn_readlane(sr.f, idx);
+                const int n = __builtin_amdgcn_readlane(sr.n, idx);
+                int r = run + below;
+#pragma unroll
+                for (int k = 0; k < K; k++) {
+                    if ((hit >> k) & 1u) {
+                        const int t = first_above(inst + f, n, r);
+                        c[k] = t < n ? inst[f + t].y : -1;
+                        r++;
+                    }
+                }
+            }
+            if (lane == idx) {
+                sr.run = run + tot;
+                if (sr.run >= sr.end) seek(sr, inst);
+            }
+        } else {
+            const int32_t base = srun[y];
+            const int f = rfirst[y], n = rcnt[y];
+            int r = base + below;
+#pragma unroll
+            for (int k = 0; k < K; k++) {
+                if ((hit >> k) & 1u) {
+                    const int t = first_above(inst + f, n, r);
+                    c[k] = t < n ? inst[f + t].y : -1;
+                    r++;
+                }
+            }
+            wave_lds_fence();
+            if (lane == 0) srun[y] = base + tot;
+            wave_lds_fence();
+        }
+        pend &= ~hit;
+    }
+}
 
 template <int W>
 __global__ __launch_bounds__(W *kWave) void reroute_kernel(
@@ -23,15 +148,16 @@ __global__ __launch_bounds__(W *kWave) void reroute_kernel(
     const int32_t *__restrict__ log2phy, const int32_t *__restrict__ logcnt,
     int32_t *__restrict__ out) {
     extern __shared__ __align__(16) unsigned char sh_raw[];
-    uint64_t *mask_all = reinterpret_cast<uint64_t *>(sh_raw);               // [W][E]
-    int32_t *run_all = reinterpret_cast<int32_t *>(mask_all + (size_t)W * E);  // [W][E]
-    int32_t *rfirst = run_all + (size_t)W * E;                                 // [E]
-    int32_t *rcnt = rfirst + E;                                                // [E]
-    int32_t *iend = rcnt + E;                                                  // [Phi]
-    int32_t *iphys = iend + Phi;                                               // [Phi]
+    int2 *inst = reinterpret_cast<int2 *>(sh_raw);                        // [Phi] (end, phys)
+    int32_t *rfirst = reinterpret_cast<int32_t *>(inst + Phi);            // [E]
+    int32_t *rcnt = rfirst + E;                                           // [E]
+    int32_t *code_all = rcnt + E;                                         // [W][E]
+    int32_t *srun_all = code_all + (size_t)W * E;                         // [W][E]
+    int32_t *sidx_all = srun_all + (size_t)W * E;                         // [W][64]
     const int wave = threadIdx.x / kWave;
     const int lane = threadIdx.x % kWave;
     const int p = blockIdx.y;
+    const int E1 = E + 1;
 
     // --- route table of this plan: instances of each expert, cumulative quotas
     if (wave == 0) {
@@ -46,11 +172,10 @@ __global__ __launch_bounds__(W *kWave) void reroute_kernel(
             const int incl = wave_incl_scan_i32(n);
             if (e < E) {
                 int start = carry + incl - n;
-                int nn = n;
-                if (start >= Phi) { start = Phi; nn = 0; }
-                else if (start + nn > Phi) nn = Phi - start;
+                if (start > Phi) start = Phi;
+                if (start + n > Phi) n = Phi - start;
                 rfirst[e] = start;
-                rcnt[e] = nn;
+                rcnt[e] = n;
             }
             carry += __shfl(incl, kWave - 1);
         }
@@ -64,67 +189,118 @@ __global__ __launch_bounds__(W *kWave) void reroute_kernel(
             const int s = row[t];
             const bool ok = s >= 0 && s < Phi;
             acc += ok ? phy_quota[(int64_t)p * Phi + s] : 0;
-            iend[f + t] = acc > 0x7fffffff ? 0x7fffffff : (acc < 0 ? 0 : (int32_t)acc);
-            iphys[f + t] = ok ? s : -1;
+            const int32_t end = acc > 0x7fffffff ? 0x7fffffff : (acc < 0 ? 0 : (int32_t)acc);
+            inst[f + t] = make_int2(end, ok ? s : -1);
         }
     }
     __syncthreads();
 
     const int64_t sb = (int64_t)blockIdx.x * W + wave;
     if (sb >= nsb) return;  // per-wave state below: no more block barriers
-    uint64_t *mask = mask_all + (size_t)wave * E;
-    int32_t *run = run_all + (size_t)wave * E;
-    const int32_t *row = ws + ((int64_t)p * nsb + sb) * (E + 1);
-    for (int e = lane; e < E; e += kWave) { run[e] = row[e]; mask[e] = 0; }
+    int32_t *code = code_all + (size_t)wave * E;
+    int32_t *srun = srun_all + (size_t)wave * E;
+    int32_t *sidx = sidx_all + (size_t)wave * kWave;
+    // --- per-expert code for this sub-block
+    const int32_t *row0 = ws + ((int64_t)p * (nsb + 1) + sb) * E1;
+    const int32_t *row1 = row0 + E1;  // next prefix row; after the last sub-block, the totals
+    int nsplit = 0;
+    for (int e0 = 0; e0 < E; e0 += kWave) {
+        const int e = e0 + lane;
+        int32_t cd = -1, run = 0;
+        if (e < E) {
+            run = row0[e];
+            const int32_t nxt = row1[e];
+            const int f = rfirst[e], n = rcnt[e];
+            const int t = first_above(inst + f, n, run);
+            if (nxt > run && t < n) cd = nxt <= inst[f + t].x ? inst[f + t].y : kSplit;
+        }
+        const bool sp = cd == kSplit;
+        const uint64_t m = __ballot(sp);
+        if (sp) {
+            const int idx = nsplit + __popcll(m & lanemask_lt());
+            if (idx < kWave) {
+                cd = (int32_t)(0x80000000u | (uint32_t)idx);
+                sidx[idx] = e;
+            } else {
+                cd = kSplitLds;
+            }
+        }
+        nsplit += __popcll(m);
+        if (e < E) { code[e] = cd; srun[e] = run; }
+    }
     wave_lds_fence();
+    SplitRegs sr{0, 0, 0, 0, 0x7fffffff, -1};
+    if (lane < nsplit) {
+        const int e = sidx[lane];
+        sr.run = srun[e];
+        sr.f = rfirst[e];
+        sr.n = rcnt[e];
+        seek(sr, inst);
+    }
 
     const int64_t begin = sb * sub;
     const int64_t end = (begin + sub < N) ? begin + sub : N;
     const int32_t *src = ids + (int64_t)p * N;
     int32_t *dst = out + (int64_t)p * N;
-    const uint64_t lt = lanemask_lt();
-    const uint64_t bit = 1ull << lane;
     const uint32_t uE = (uint32_t)E;
-    constexpr int U = 8;
-    for (int64_t g = begin; g < end; g += U * kWave) {
-        int32_t v[U];
+    int64_t g = begin;
+
+    // 16-byte path over whole 256-pair tiles
+    if ((((uintptr_t)(src + begin) | (uintptr_t)(dst + begin)) & 15) == 0) {
+        constexpr int U = EP_RR_UNROLL;
+        const int64_t ntile = (end - begin) / (4 * kWave);
+        const i32x4 *s4 = reinterpret_cast<const i32x4 *>(src + begin);
+        i32x4 *d4 = reinterpret_cast<i32x4 *>(dst + begin);
+        int64_t tt = 0;
+        for (; tt + U <= ntile; tt += U) {
+            i32x4 v[U];
 #pragma unroll
-        for (int u = 0; u < U; u++) {
-            const int64_t i = g + u * kWave + lane;
-            v[u] = i < end ? __builtin_nontemporal_load(src + i) : -1;
-        }
+            for (int u = 0; u < U; u++) v[u] = __builtin_nontemporal_load(s4 + (tt + u) * kWave + lane);
 #pragma unroll
-        for (int u = 0; u < U; u++) {
-            const int32_t x = v[u];
-            const bool valid = (uint32_t)x < uE;
-            if (valid) atomicOr(reinterpret_cast<unsigned long long *>(&mask[x]), bit);
-            wave_lds_fence();
-            uint64_t m = 0;
-            int32_t base = 0;
-            if (valid) { m = mask[x]; base = run[x]; }
-            wave_lds_fence();
-            const uint64_t below = m & lt;
-            int32_t phys = -1;
-            if (valid) {
-                if (below == 0) { run[x] = base + (int32_t)__popcll(m); mask[x] = 0; }
-                const int32_t j = base + (int32_t)__popcll(below);
-                const int f = rfirst[x], n = rcnt[x];
-                int lo = 0, hi = n;
-                while (lo < hi) {
-                    const int mid = (lo + hi) >> 1;
-                    if (j < iend[f + mid]) hi = mid; else lo = mid + 1;
+            for (int u = 0; u < U; u++) {
+                int32_t x[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+                int32_t c[4];
+                bool sp = false;
+#pragma unroll
+                for (int k = 0; k < 4; k++) {
+                    c[k] = (uint32_t)x[k] < uE ? code[x[k]] : -1;
+                    sp |= is_split(c[k]);
                 }
-                phys = lo < n ? iphys[f + lo] : -1;
+                if (__ballot(sp)) resolve_split<4>(x, c, sr, rfirst, rcnt, inst, srun);
+                i32x4 o;
+                o.x = c[0]; o.y = c[1]; o.z = c[2]; o.w = c[3];
+                __builtin_nontemporal_store(o, d4 + (tt + u) * kWave + lane);
             }
-            const int64_t i = g + u * kWave + lane;
-            if (i < end) __builtin_nontemporal_store(phys, dst + i);
-            wave_lds_fence();
         }
+        for (; tt < ntile; tt++) {
+            const i32x4 v = __builtin_nontemporal_load(s4 + tt * kWave + lane);
+            int32_t x[4] = {v.x, v.y, v.z, v.w};
+            int32_t c[4];
+            bool sp = false;
+#pragma unroll
+            for (int k = 0; k < 4; k++) {
+                c[k] = (uint32_t)x[k] < uE ? code[x[k]] : -1;
+                sp |= is_split(c[k]);
+            }
+            if (__ballot(sp)) resolve_split<4>(x, c, sr, rfirst, rcnt, inst, srun);
+            i32x4 o;
+            o.x = c[0]; o.y = c[1]; o.z = c[2]; o.w = c[3];
+            __builtin_nontemporal_store(o, d4 + tt * kWave + lane);
+        }
+        g = begin + ntile * 4 * kWave;
+    }
+    // one pair per lane for the rest (tail, or rows not 16-byte aligned)
+    for (; g < end; g += kWave) {
+        const int64_t i = g + lane;
+        int32_t x[1] = {i < end ? src[i] : -1};
+        int32_t c[1] = {(uint32_t)x[0] < uE ? code[x[0]] : -1};
+        if (__ballot(is_split(c[0]))) resolve_split<1>(x, c, sr, rfirst, rcnt, inst, srun);
+        if (i < end) dst[i] = c[0];
     }
 }
 
 int pick_waves(int E, int Phi) {
-    for (int w = 4; w >= 1; w >>= 1)
+    for (int w = EP_RR_MAX_WAVES; w >= 1; w >>= 1)
         if (reroute_lds_bytes(E, Phi, w) <= 65536) return w;
     return 0;
 }
@@ -132,7 +308,7 @@ int pick_waves(int E, int Phi) {
 }  // namespace
 
 size_t reroute_lds_bytes(int E, int Phi, int waves) {
-    return (size_t)waves * E * 12 + (size_t)E * 8 + (size_t)Phi * 8;
+    return (size_t)Phi * 8 + (size_t)E * 8 + (size_t)waves * (E * 8 + kWave * 4);
 }
 
 hipError_t launch_reroute(const int32_t *ids, int64_t N, int32_t P, const ep_layout_t &L,
@@ -146,6 +322,10 @@ hipError_t launch_reroute(const int32_t *ids, int64_t N, int32_t P, const ep_lay
     const size_t lds = reroute_lds_bytes(E, Phi, w);
     dim3 grid((unsigned)((nsb + w - 1) / w), (unsigned)P);
     switch (w) {
+        case 8:
+            hipLaunchKernelGGL(reroute_kernel<8>, grid, dim3(8 * kWave), lds, s, ids, N, E, Phi,
+                               rho, sub, nsb, ws, phy_quota, log2phy, logcnt, out);
+            break;
         case 4:
             hipLaunchKernelGGL(reroute_kernel<4>, grid, dim3(4 * kWave), lds, s, ids, N, E, Phi,
                                rho, sub, nsb, ws, phy_quota, log2phy, logcnt, out);

@@ -9,9 +9,29 @@
 namespace ep {
 namespace {
 
-constexpr int kFillThreads = 256;
-constexpr int kFillUnroll = 4;
-constexpr int64_t kFillChunk = (int64_t)kFillThreads * kFillUnroll * 4;  // 16-byte vectors
+#ifndef EP_FILL_THREADS
+#define EP_FILL_THREADS 256
+#endif
+#ifndef EP_FILL_UNROLL
+#define EP_FILL_UNROLL 4
+#endif
+#ifndef EP_FILL_CHUNK_ITERS
+#define EP_FILL_CHUNK_ITERS 1
+#endif
+#ifndef EP_FILL_NT
+#define EP_FILL_NT 0
+#endif
+constexpr int kFillThreads = EP_FILL_THREADS;
+constexpr int kFillUnroll = EP_FILL_UNROLL;
+constexpr int64_t kFillChunk = (int64_t)kFillThreads * kFillUnroll * EP_FILL_CHUNK_ITERS;  // 16-byte vectors
+
+#if EP_FILL_NT
+#define LD(p) __builtin_nontemporal_load(p)
+#define ST(v, p) __builtin_nontemporal_store(v, p)
+#else
+#define LD(p) (*(p))
+#define ST(v, p) (*(p) = (v))
+#endif
 
 __global__ __launch_bounds__(kFillThreads) void slot_fill_kernel(
     const u32x4 *__restrict__ w, int64_t vpe, int32_t E, const int32_t *__restrict__ phy2log,
@@ -27,11 +47,11 @@ __global__ __launch_bounds__(kFillThreads) void slot_fill_kernel(
     for (; i + (kFillUnroll - 1) * kFillThreads < c1; i += kFillUnroll * kFillThreads) {
         u32x4 x[kFillUnroll];
 #pragma unroll
-        for (int u = 0; u < kFillUnroll; u++) x[u] = __builtin_nontemporal_load(src + i + u * kFillThreads);
+        for (int u = 0; u < kFillUnroll; u++) x[u] = LD(src + i + u * kFillThreads);
 #pragma unroll
-        for (int u = 0; u < kFillUnroll; u++) __builtin_nontemporal_store(x[u], dst + i + u * kFillThreads);
+        for (int u = 0; u < kFillUnroll; u++) ST(x[u], dst + i + u * kFillThreads);
     }
-    for (; i < c1; i += kFillThreads) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+    for (; i < c1; i += kFillThreads) ST(LD(src + i), dst + i);
 }
 
 }  // namespace

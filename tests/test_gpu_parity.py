@@ -335,3 +335,61 @@ def test_deterministic_and_stream_independent(dev):
         assert torch.equal(a[k], b[k]), k
     assert torch.equal(a["plan"].log2phy, b["plan"].log2phy)
     assert torch.equal(a["plan"].phy_quota, b["plan"].phy_quota)
+
+
+# ------------------------------------------------ planner kernel selection
+# The library plans with one rank per lane when R <= 64 and every rank has at
+# most 16 spare slots (1, 2, 4, 8 or 16 spare registers per lane), and with the
+# generic LDS kernel otherwise; both must agree with the oracle.
+@pytest.mark.parametrize("R,E,max_sp", [(8, 20, 1), (16, 40, 2), (24, 50, 3), (32, 64, 7),
+                                        (12, 30, 13), (70, 140, 1), (90, 90, 0), (4, 12, 20)])
+def test_plan_kernel_paths(dev, R, E, max_sp):
+    rng = np.random.default_rng(R * 1000 + E)
+    nc = np.full(R, E // R)
+    nc[: E % R] += 1
+    ne = rng.permutation(E)
+    sc = rng.integers(0, max_sp + 1, size=R)
+    sc[0] = max_sp
+    S = int(sc.sum())
+    if min(R, 1 + S) > 64:                      # keep rho within the planner's limit
+        sc[:] = 0
+        sc[: 63] = 1
+    lay_o = oracle.Layout.of(E, R, nc, ne, sc)
+    P = 5
+    loads = (rng.pareto(0.7, size=(P, E)) * 100).astype(np.int32)
+    loads[0] = 0
+    loads[1, rng.integers(0, E)] = 10**6
+    refs = [oracle.plan(l, lay_o) for l in loads]
+    print(f"[plan-path] R={R} E={E} max_spare={int(sc.max())} steps={[r.steps for r in refs]}", flush=True)
+    lay = ep.Layout.create(E, nc, ne, sc, device=dev)
+    status = torch.zeros(P, dtype=torch.int32, device=dev)
+    out = ep.ep_plan_quota(torch.from_numpy(loads).to(dev), lay, status=status)
+    torch.cuda.synchronize()
+    _assert_plan_equal(out, refs)
+    np.testing.assert_array_equal(_np(status), [ep.EP_STATUS_STEP_CAP if r.cap_hit else 0 for r in refs])
+
+
+def test_reroute_many_split_experts_in_one_subblock(dev):
+    # 200 experts on 64 ranks with 3 spare slots each; experts 0..119 carry 60
+    # pairs, the rest 1: the whole plan (7280 pairs) is one sub-block and more
+    # than 64 replicated experts have a quota boundary inside it (the reroute
+    # keeps 64 of them in registers and the rest in LDS)
+    E, R = 200, 64
+    nc = [4] * 8 + [3] * 56
+    lay_o = oracle.Layout.of(E, R, nc, list(range(E)), [3] * R)
+    rng = np.random.default_rng(21)
+    cnt = np.where(np.arange(E) < 120, 60, 1)
+    ids = rng.permutation(np.repeat(np.arange(E), cnt)).astype(np.int32)[None]
+    ld, _ = oracle.histogram(ids[0], E)
+    pl = oracle.plan(ld, lay_o)
+    n_split = int(np.sum((pl.logcnt >= 2) & (ld > 0)))
+    print(f"[many-split] replicated experts = {n_split}", flush=True)
+    assert n_split > 64
+    lay = ep.Layout.create(E, nc, list(range(E)), [3] * R, device=dev)
+    d_ids = torch.from_numpy(ids).to(dev)
+    _, ws, _ = ep.ep_load_histogram(d_ids, lay)
+    phys = ep.ep_reroute(d_ids, lay, torch.from_numpy(pl.phy_quota[None]).to(dev),
+                         torch.from_numpy(pl.log2phy[None]).to(dev), torch.from_numpy(pl.logcnt[None]).to(dev), ws)
+    torch.cuda.synchronize()
+    ref, _ = oracle.reroute(ids[0], E, pl.phy_quota, pl.log2phy, pl.logcnt)
+    np.testing.assert_array_equal(_np(phys[0]), ref)
