@@ -41,7 +41,7 @@ METRIC = "(token,k) pairs/s via hist+plan+reroute; plan µs/layer at EP64; HBM G
 # HBM bytes per slot-fill launch measured with rocprofv3 --pmc (FETCH_SIZE and
 # WRITE_SIZE), scaled by the same counters on a plain copy of known size; valid
 # only for the kernel source they were taken on.
-TRAFFIC = None
+TRAFFIC = {"kernel_sha": "bd13ef8067a89f47", "fetch_kib": 1145030.5, "write_kib": 2290666.4, "fetch_scale": 2.0, "write_scale": 1.0, "bytes_per_launch": 4690610216}
 
 
 def _src_sha(name: str) -> str:
@@ -85,6 +85,8 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", default="qwen3_235b")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work (0 = skip)")
     ap.add_argument("--latency-reps", type=int, default=30)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -96,6 +98,17 @@ def main(argv=None) -> int:
         return 2
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        # one elementwise kernel that reads and writes 1 GiB each (a plain copy
+        # with a sign flip; torch's own contiguous copy is a DMA, not a kernel)
+        n = 1 << 28
+        src = torch.empty(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "launches": 3}))
+        return 0
     wl = W.get(args.workload)
     P, N, E, S = wl.num_plans, wl.pairs_per_plan, wl.num_experts, wl.num_spare
     bpe = wl.bytes_per_expert

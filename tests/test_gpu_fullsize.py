@@ -1,0 +1,97 @@
+"""Full-size parity: every workload at its full size, all plans in one launch
+(the launch configuration bench.py times), against the CPU oracle.
+
+Histogram, plan, reroute and statistics are compared in full; the slot fill
+(gigabytes per layer) is compared on sampled 16-byte-aligned windows of every
+used spare slot, and empty slots must keep their sentinel bytes.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+ep = pytest.importorskip("moe_expert_load_layer_amd")
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+@pytest.mark.parametrize("name", W.WORKLOAD_ORDER)
+def test_fullsize_path(dev, name):
+    wl = W.get(name)
+    print(f"[fullsize] {name}: P={wl.num_plans} N={wl.pairs_per_plan}", flush=True)
+    ids = W.make_ids(wl, device=dev)
+    lay = ep.Layout.from_workload(wl, device=dev)
+    out = ep.run_path(ids, lay)
+    torch.cuda.synchronize()
+    ids_h = ids.cpu().numpy()
+    del ids
+    load = out["load"].cpu().numpy()
+    phys = out["phys"].cpu().numpy()
+    st = out["stats"].cpu().numpy()
+    imb = out["imbalance"].cpu().numpy()
+    status = out["status"].cpu().numpy()
+    plan = {k: getattr(out["plan"], k).cpu().numpy() for k in ("phy2log", "phy_quota", "logcnt", "log2phy", "steps")}
+    del out
+    torch.cuda.empty_cache()
+    lay_o = oracle.Layout.from_workload(wl)
+    for p in range(wl.num_plans):
+        ld, bad = oracle.histogram(ids_h[p], wl.num_experts)
+        assert np.array_equal(load[p], ld), f"load plan {p}"
+        pl = oracle.plan(ld, lay_o)
+        assert np.array_equal(plan["phy2log"][p], pl.phy2log), f"phy2log plan {p}"
+        assert np.array_equal(plan["phy_quota"][p], pl.phy_quota), f"quota plan {p}"
+        assert np.array_equal(plan["logcnt"][p], pl.logcnt), f"logcnt plan {p}"
+        assert np.array_equal(plan["log2phy"][p], pl.log2phy), f"log2phy plan {p}"
+        assert plan["steps"][p] == pl.steps
+        assert status[p] == (ep.EP_STATUS_STEP_CAP if pl.cap_hit else 0) | (ep.EP_STATUS_BAD_ID if bad else 0)
+        ph, _ = oracle.reroute(ids_h[p], wl.num_experts, pl.phy_quota, pl.log2phy, pl.logcnt)
+        assert np.array_equal(phys[p], ph), f"reroute plan {p}"
+        s = oracle.stats(ld, pl.phy_quota, lay_o)
+        assert np.array_equal(st[p], s.as_row()), f"stats plan {p}"
+        assert imb[p].tolist() == [s.imbalance_before, s.imbalance_after]
+
+
+@pytest.mark.parametrize("name", W.WORKLOAD_ORDER)
+def test_fullsize_slot_fill(dev, name):
+    wl = W.get(name)
+    print(f"[fullsize-fill] {name}: E={wl.num_experts} S={wl.num_spare} bytes/expert={wl.bytes_per_expert}",
+          flush=True)
+    lay = ep.Layout.from_workload(wl, device=dev)
+    lay_o = oracle.Layout.from_workload(wl)
+    _, _, _, spare = lay_o.slots()
+    plans = [0, wl.num_plans - 1]
+    ids = W.make_ids(wl, device=dev, plans=plans)
+    weights = W.make_weights(wl, device=dev)
+    w16 = weights.view(torch.int16)
+    slot = torch.empty((wl.num_spare, weights.shape[1]), dtype=weights.dtype, device=dev)
+    s16 = slot.view(torch.int16)
+    rng = np.random.default_rng(5)
+    elems = weights.shape[1]
+    win = 2048                                  # int16 elements per window (4 KiB)
+    for i, p in enumerate(plans):
+        ld, _ = oracle.histogram(ids[i].cpu().numpy(), wl.num_experts)
+        pl = oracle.plan(ld, lay_o)
+        s16.fill_(0x7FC1)
+        ep.ep_slot_fill(weights, torch.from_numpy(pl.phy2log).to(dev), lay, slot)
+        torch.cuda.synchronize()
+        for o, s in enumerate(spare):
+            e = int(pl.phy2log[s])
+            starts = list(rng.integers(0, max(1, elems - win), size=6) // 8 * 8) + [0, max(0, elems - win)]
+            for a in starts:
+                got = s16[o, a:a + win].cpu().numpy()
+                if e >= 0:
+                    exp = w16[e, a:a + win].cpu().numpy()
+                    assert np.array_equal(got, exp), f"plan {p} slot {o} expert {e} window {a}"
+                else:
+                    assert np.all(got == 0x7FC1), f"plan {p} empty slot {o} was written"
+    del weights, slot
+    torch.cuda.empty_cache()
