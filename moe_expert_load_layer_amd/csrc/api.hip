@@ -143,10 +143,10 @@ int ep_plan_quota(const int32_t *load, int32_t P, const ep_layout_t *layout, int
     if (!layout_ok(layout) || !load || !phy2log || !phy_quota || !logcnt || !log2phy)
         return EP_ERR_INVALID_ARG;
     if (P < 1 || P > kMaxPlans || layout->max_replicas > 64) return EP_ERR_INVALID_ARG;
-    const int spr = plan_lanes_spr(*layout, layout->max_rank_spares, layout->max_rank_natives);
-    if (spr == 0 && plan_lds_bytes(*layout) > kMaxLds) return EP_ERR_INVALID_ARG;
+    const int cfg = plan_lanes_cfg(*layout);
+    if (cfg == 0 && plan_lds_bytes(*layout) > kMaxLds) return EP_ERR_INVALID_ARG;
     return hip_rc(launch_plan(load, P, *layout, phy2log, phy_quota, logcnt, log2phy, steps, status,
-                              as_stream(stream), spr));
+                              as_stream(stream), cfg));
 }
 
 int ep_reroute(const int32_t *topk_ids, int64_t N, int32_t P, const ep_layout_t *layout,

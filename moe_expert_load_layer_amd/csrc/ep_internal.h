@@ -186,13 +186,13 @@ __device__ __forceinline__ void wave_lds_fence() {
 hipError_t launch_histogram(const int32_t *ids, int64_t N, int32_t P, int32_t E, int64_t sub,
                             int64_t nsb, int32_t *ws, int32_t *load, uint32_t *status,
                             hipStream_t s);
-// spr > 0 selects the rank-per-lane planner with that many spare registers per
-// lane (see plan_lanes_spr); spr == 0 selects the generic planner
+// cfg > 0 selects the rank-per-lane planner (32 * natives + spares registers
+// per lane, see plan_lanes_cfg); cfg == 0 selects the generic planner
 hipError_t launch_plan(const int32_t *load, int32_t P, const ep_layout_t &L, int32_t *phy2log,
                        int32_t *phy_quota, int32_t *logcnt, int32_t *log2phy, int32_t *steps,
-                       uint32_t *status, hipStream_t s, int spr);
+                       uint32_t *status, hipStream_t s, int cfg);
 size_t plan_lds_bytes(const ep_layout_t &L);
-int plan_lanes_spr(const ep_layout_t &L, int max_spare_per_rank, int max_native_per_rank);
+int plan_lanes_cfg(const ep_layout_t &L);
 hipError_t launch_reroute(const int32_t *ids, int64_t N, int32_t P, const ep_layout_t &L,
                           int64_t sub, int64_t nsb, const int32_t *ws, const int32_t *phy_quota,
                           const int32_t *log2phy, const int32_t *logcnt, int32_t *out,

@@ -258,23 +258,28 @@ __global__ __launch_bounds__(kWave) void plan_kernel_generic(const int32_t *__re
 
 
 // ---------------------------------------------------------------------------
-// Rank-per-lane planner (R <= 64, at most SPR spare slots per rank).
+// Rank-per-lane planner (R <= 64, at most NPR native experts and SPR spare
+// slots per rank).
 //
-// Lane r owns rank r: its load, its free spare count and the owner and quota
-// of each of its spare slots live in registers.  The instances of an expert
-// are then found lane-locally (native rank, or a spare slot of the lane that
-// holds the expert), the water-fill runs over the lanes that host the expert,
-// and a commit only touches those lanes' registers plus the native quota in
-// LDS.  Cross-lane steps are DPP reductions, ballots and readlanes.
+// Lane r owns rank r.  In registers: its load, free spare count, its native
+// experts (ID, load, quota, instance count) and its spare slots (owner,
+// quota).  Candidates on the hottest rank come from that lane's registers by
+// readlane; the instances of an expert are found lane-locally (its native
+// lane, or a lane holding it in a spare slot); the water-fill runs over the
+// lanes that host the expert and a commit only touches their registers.  LDS
+// holds the static (native rank, native index) of every expert and, at the
+// end, the per-expert masks of replica ranks used to order log2phy.
 // ---------------------------------------------------------------------------
-struct ExpertInfo {
-    int32_t nq;     // quota of the native instance
-    int32_t icnt;   // instances (native + replicas)
-    int32_t load;   // the expert's load
-    int32_t nrank;  // rank of the native instance
-};
+template <int N>
+__device__ __forceinline__ int32_t pick(const int32_t (&v)[N], int i) {
+    int32_t r = v[0];
+#pragma unroll
+    for (int k = 1; k < N; k++)
+        if (i == k) r = v[k];
+    return r;
+}
 
-template <int SPR>
+template <int NPR, int SPR>
 __global__ __launch_bounds__(kWave) void plan_kernel_lanes(const int32_t *__restrict__ load, PlanArgs a,
                                                            int32_t *__restrict__ phy2log,
                                                            int32_t *__restrict__ phy_quota,
@@ -284,33 +289,41 @@ __global__ __launch_bounds__(kWave) void plan_kernel_lanes(const int32_t *__rest
                                                            uint32_t *__restrict__ status) {
     const int E = a.E, R = a.R, Phi = a.Phi, S = a.S, rho = a.rho;
     extern __shared__ __align__(16) unsigned char sh_raw[];
-    ExpertInfo *info = reinterpret_cast<ExpertInfo *>(sh_raw);           // [E]
-    uint64_t *emask = reinterpret_cast<uint64_t *>(info + E);             // [E]
-    int32_t *shome = reinterpret_cast<int32_t *>(emask + E);              // [Phi]
+    uint64_t *emask = reinterpret_cast<uint64_t *>(sh_raw);      // [E] ranks of live replicas
+    int32_t *nri = reinterpret_cast<int32_t *>(emask + E);       // [E] native rank << 8 | index
 
     const int p = blockIdx.x;
     const int lane = threadIdx.x;
     const int32_t *lp = load + (int64_t)p * E;
 
-    for (int s = lane; s < Phi; s += kWave) shome[s] = a.T.slot_home[s];
-    for (int e = lane; e < E; e += kWave) {
-        const int l = lp[e];
-        info[e] = ExpertInfo{l, 1, l, a.T.slot_rank[a.T.home_slot[e]]};
-        emask[e] = 0;
-    }
-    // rank-lane registers
     const bool is_rank = lane < R;
     const int f0 = is_rank ? a.T.rank_first[lane] : 0;
     const int nat = is_rank ? a.T.rank_nat[lane] : 0;
     const int spc = is_rank ? a.T.rank_first[lane + 1] - f0 - nat : 0;
     int freec = spc;
-    int sp_owner[SPR], sp_q[SPR];
+    // bit i: native i, bit NPR + j: spare j of this rank.  Set when another
+    // expert's move changed this rank's load after the slot's expert was last
+    // water-filled; a re-level of an expert whose slots are all clean would
+    // reproduce its current quotas, so it is skipped.
+    uint32_t dirty = 0;
+    int32_t nat_e[NPR], nat_ld[NPR], nat_q[NPR], nat_ic[NPR];
+    int32_t sp_owner[SPR], sp_q[SPR];
+#pragma unroll
+    for (int i = 0; i < NPR; i++) nat_e[i] = i < nat ? a.T.slot_home[f0 + i] : -1;
+#pragma unroll
+    for (int i = 0; i < NPR; i++) {
+        nat_ld[i] = nat_e[i] >= 0 ? lp[nat_e[i]] : 0;
+        nat_q[i] = nat_ld[i];
+        nat_ic[i] = 1;
+        if (nat_e[i] >= 0) nri[nat_e[i]] = (lane << 8) | i;
+    }
 #pragma unroll
     for (int j = 0; j < SPR; j++) { sp_owner[j] = -1; sp_q[j] = 0; }
-    __syncthreads();
+    for (int e = lane; e < E; e += kWave) emask[e] = 0;
     int rl = 0;
-    for (int i = 0; i < nat; i++) rl += info[shome[f0 + i]].load;
-    if (!is_rank) rl = 0;
+#pragma unroll
+    for (int i = 0; i < NPR; i++) rl += nat_ld[i];
+    __syncthreads();
 
     const int cap = 2 * S + R;
     int steps = 0, cap_hit = 0;
@@ -321,20 +334,22 @@ __global__ __launch_bounds__(kWave) void plan_kernel_lanes(const int32_t *__rest
         const int h = __ffsll((long long)__ballot(is_rank && rl == vmax)) - 1;
         const int Lh = vmax;
 
-        // candidates: h's natives in lanes [0, nat_h), h's spare slots after them
-        const int nat_h = __builtin_amdgcn_readlane(nat, h);
-        const int f0_h = __builtin_amdgcn_readlane(f0, h);
-        int ce = -1, cq = 0;
-        if (lane < nat_h) ce = shome[f0_h + lane];
+        // candidates: h's natives in lanes [0, NPR), h's spare slots in [NPR, NPR+SPR)
+        int ce = -1, cq = 0, cld = 0, cic = 2, cnr = -1, cidx = 0;
+#pragma unroll
+        for (int i = 0; i < NPR; i++) {
+            const int e = __builtin_amdgcn_readlane(nat_e[i], h);
+            const int q = __builtin_amdgcn_readlane(nat_q[i], h);
+            const int l = __builtin_amdgcn_readlane(nat_ld[i], h);
+            const int ic = __builtin_amdgcn_readlane(nat_ic[i], h);
+            if (lane == i) { ce = e; cq = q; cld = l; cic = ic; cnr = h; cidx = i; }
+        }
 #pragma unroll
         for (int j = 0; j < SPR; j++) {
-            const int oe = __builtin_amdgcn_readlane(sp_owner[j], h);
-            const int oq = __builtin_amdgcn_readlane(sp_q[j], h);
-            if (lane == nat_h + j) { ce = oe; cq = oq; }
+            const int e = __builtin_amdgcn_readlane(sp_owner[j], h);
+            const int q = __builtin_amdgcn_readlane(sp_q[j], h);
+            if (lane == NPR + j) { ce = e; cq = q; }
         }
-        ExpertInfo ci{0, 0, 0, 0};
-        if (ce >= 0) ci = info[ce];
-        if (lane < nat_h) cq = ci.nq;
         const bool valid = ce >= 0 && cq > 0;
         const uint64_t key = valid ? (((uint64_t)(uint32_t)cq << 32) | inv((uint32_t)ce)) : 0;
         // order of the candidates: count the larger keys
@@ -351,11 +366,19 @@ __global__ __launch_bounds__(kWave) void plan_kernel_lanes(const int32_t *__rest
         for (int pass = 0; pass < 2 && !committed; pass++) {
             for (int c = 0; c < nc && !committed; c++) {
                 const int cl = __ffsll((long long)__ballot(valid && crank == c)) - 1;
+                if (pass == 0 && __builtin_amdgcn_readlane(cic, cl) < 2) continue;
                 const int e = __builtin_amdgcn_readlane(ce, cl);
-                if (pass == 0 && __builtin_amdgcn_readlane(ci.icnt, cl) < 2) continue;
-                const int T = __builtin_amdgcn_readlane(ci.load, cl);
-                const int nr = __builtin_amdgcn_readlane(ci.nrank, cl);
-                const int nqe = __builtin_amdgcn_readlane(ci.nq, cl);
+                int nr = __builtin_amdgcn_readlane(cnr, cl);
+                int idx, T;
+                if (nr >= 0) {
+                    idx = __builtin_amdgcn_readlane(cidx, cl);
+                    T = __builtin_amdgcn_readlane(cld, cl);
+                } else {
+                    const int packed = nri[e];
+                    nr = __builtin_amdgcn_readfirstlane(packed >> 8);
+                    idx = __builtin_amdgcn_readfirstlane(packed & 0xff);
+                    T = __builtin_amdgcn_readlane(pick(nat_ld, idx), nr);
+                }
                 const bool replicate = pass == 1;
 
                 // instances of e on this lane's rank
@@ -368,8 +391,10 @@ __global__ __launch_bounds__(kWave) void plan_kernel_lanes(const int32_t *__rest
 #pragma unroll
                 for (int j = 0; j < SPR; j++)
                     if (j == jr) q = sp_q[j];
-                if (nat_here) q = nqe;
+                if (nat_here) q = pick(nat_q, idx);
                 const bool inst = nat_here || jr >= 0;
+                const uint32_t mine = (nat_here ? 1u << idx : 0u) | (jr >= 0 ? 1u << (NPR + jr) : 0u);
+                if (!replicate && !__ballot((dirty & mine) != 0)) continue;
                 const int b = rl - q;
                 bool isnew = false;
                 if (replicate) {
@@ -382,30 +407,37 @@ __global__ __launch_bounds__(kWave) void plan_kernel_lanes(const int32_t *__rest
                 const bool act = inst || isnew;
                 // sorted position by (background, rank) and inclusive prefix sum
                 int pos = 0;
-                int64_t Sinc = T;
+                uint32_t Sinc = (uint32_t)T;
                 for (uint64_t mm = __ballot(act); mm; mm &= mm - 1) {
                     const int j = __ffsll((long long)mm) - 1;
                     const int bj = __builtin_amdgcn_readlane(b, j);
                     const bool less = bj < b || (bj == b && j < lane);
                     pos += less ? 1 : 0;
-                    if (less || j == lane) Sinc += bj;
+                    if (less || j == lane) Sinc += (uint32_t)bj;
                 }
                 // the filled instances form a prefix of the sorted order, so
                 // m* = number of instances with m*b_(m) < S_m
-                const int mstar = __popcll(__ballot(act && (int64_t)(pos + 1) * b < Sinc));
+                const int mstar = __popcll(__ballot(act && (uint64_t)(pos + 1) * (uint32_t)b < Sinc));
                 int qn = 0;
                 if (mstar > 0) {
                     const int ls = __ffsll((long long)__ballot(act && pos == mstar - 1)) - 1;
-                    const uint32_t Ss = (uint32_t)readlane_i64(Sinc, ls);
+                    const uint32_t Ss = (uint32_t)__builtin_amdgcn_readlane((int)Sinc, ls);
                     const uint32_t base = Ss / (uint32_t)mstar;
                     const uint32_t rem = Ss - (uint32_t)mstar * base;
                     if (act && pos < mstar) qn = (int)base - b + ((uint32_t)pos < rem ? 1 : 0);
                 }
                 const int newLh = __builtin_amdgcn_readlane(act ? b + qn : rl, h);
                 if (newLh >= Lh) continue;
-                // commit (lane-local, plus the native quota and count in LDS)
-                if (act) rl = b + qn;
-                if (nat_here) info[e].nq = qn;
+                // commit (lane-local)
+                if (act) {
+                    rl = b + qn;
+                    dirty = ~0u;
+                }
+                if (nat_here) {
+#pragma unroll
+                    for (int i = 0; i < NPR; i++)
+                        if (i == idx) { nat_q[i] = qn; if (replicate) nat_ic[i] += 1; }
+                }
 #pragma unroll
                 for (int j = 0; j < SPR; j++)
                     if (j == jr) sp_q[j] = qn;
@@ -414,10 +446,10 @@ __global__ __launch_bounds__(kWave) void plan_kernel_lanes(const int32_t *__rest
 #pragma unroll
                     for (int j = 0; j < SPR; j++)
                         if (j == jn) { sp_owner[j] = e; sp_q[j] = qn; }
+                    dirty &= ~(1u << (NPR + jn));
                     freec -= 1;
-                    info[e].icnt += 1;
                 }
-                wave_lds_fence();
+                if (act) dirty &= ~mine;
                 committed = true;
             }
         }
@@ -432,13 +464,25 @@ __global__ __launch_bounds__(kWave) void plan_kernel_lanes(const int32_t *__rest
         if (j < spc && sp_owner[j] >= 0)
             atomicOr(reinterpret_cast<unsigned long long *>(&emask[sp_owner[j]]), 1ull << lane);
     }
-    __syncthreads();
-
     int32_t *o_p2l = phy2log + (int64_t)p * Phi;
     int32_t *o_q = phy_quota + (int64_t)p * Phi;
     int32_t *o_l2p = log2phy + (int64_t)p * E * rho;
-    // spare slots: owner, quota and place in the owner's log2phy row
-    // (instances are one per rank, so ascending slot = ascending rank)
+    for (int64_t i = lane; i < (int64_t)E * rho; i += kWave) o_l2p[i] = -1;   // coalesced padding
+    __syncthreads();
+
+    const uint64_t below_me = (1ull << lane) - 1;
+#pragma unroll
+    for (int i = 0; i < NPR; i++) {
+        if (i < nat) {
+            const int e = nat_e[i];
+            const int s = f0 + i;
+            const uint64_t m = emask[e];
+            o_p2l[s] = e;
+            o_q[s] = nat_q[i];
+            logcnt[(int64_t)p * E + e] = 1 + __popcll(m);
+            o_l2p[(int64_t)e * rho + __popcll(m & below_me)] = s;
+        }
+    }
 #pragma unroll
     for (int j = 0; j < SPR; j++) {
         if (j < spc) {
@@ -447,25 +491,11 @@ __global__ __launch_bounds__(kWave) void plan_kernel_lanes(const int32_t *__rest
             o_p2l[s] = e;
             o_q[s] = e >= 0 ? sp_q[j] : 0;
             if (e >= 0) {
-                const uint64_t below = emask[e] & ((1ull << lane) - 1);
-                const int pos = __popcll(below) + (info[e].nrank < lane ? 1 : 0);
+                const int nr = nri[e] >> 8;
+                const int pos = __popcll(emask[e] & below_me) + (nr < lane ? 1 : 0);
                 o_l2p[(int64_t)e * rho + pos] = s;
             }
         }
-    }
-    // natives, counts, native position and padding
-    for (int e = lane; e < E; e += kWave) {
-        const ExpertInfo in = info[e];
-        const uint64_t m = emask[e];
-        const int hs = a.T.home_slot[e];
-        o_p2l[hs] = e;
-        o_q[hs] = in.nq;
-        const int cnt = 1 + __popcll(m);
-        logcnt[(int64_t)p * E + e] = cnt;
-        const int npos = __popcll(m & ((1ull << in.nrank) - 1));
-        int32_t *row = o_l2p + (int64_t)e * rho;
-        row[npos] = hs;
-        for (int t = cnt; t < rho; t++) row[t] = -1;
     }
     if (lane == 0) {
         if (steps_out) steps_out[p] = steps;
@@ -480,31 +510,41 @@ size_t plan_lds_bytes(const ep_layout_t &L) {
     return 8 * E + 8 * kWave + 4 * (5 * R + 1 + 3 * Phi + 5 * E + S + kWave);
 }
 
-static size_t lanes_lds_bytes(const ep_layout_t &L) {
-    return (size_t)L.num_experts * (sizeof(ExpertInfo) + 8) + (size_t)L.num_phys * 4;
+static size_t lanes_lds_bytes(const ep_layout_t &L) { return (size_t)L.num_experts * 12; }
+
+static int pow2_at_least(int x) {
+    int v = 1;
+    while (v < x) v <<= 1;
+    return v;
 }
 
-int plan_lanes_spr(const ep_layout_t &L, int max_spare_per_rank, int max_native_per_rank) {
+int plan_lanes_cfg(const ep_layout_t &L) {
     if (L.num_ranks > kWave) return 0;
-    int spr = 1;
-    while (spr < max_spare_per_rank) spr <<= 1;
-    if (spr > 16 || max_native_per_rank + spr > kWave) return 0;
-    if (lanes_lds_bytes(L) > 65536) return 0;
-    return spr;
+    const int npr = pow2_at_least(L.max_rank_natives > 0 ? L.max_rank_natives : 1);
+    const int spr = pow2_at_least(L.max_rank_spares > 0 ? L.max_rank_spares : 1);
+    if (npr > 8 || spr > 16 || lanes_lds_bytes(L) > 65536) return 0;
+    return npr * 32 + spr;
 }
+
+#define EP_LANES_CASE(NP, SP)                                                                   \
+    case NP * 32 + SP:                                                                          \
+        hipLaunchKernelGGL((plan_kernel_lanes<NP, SP>), g, b, lds, s, load, a, phy2log, phy_quota, \
+                           logcnt, log2phy, steps, status);                                     \
+        break;
+#define EP_LANES_ROW(NP) EP_LANES_CASE(NP, 1) EP_LANES_CASE(NP, 2) EP_LANES_CASE(NP, 4) \
+    EP_LANES_CASE(NP, 8) EP_LANES_CASE(NP, 16)
 
 hipError_t launch_plan(const int32_t *load, int32_t P, const ep_layout_t &L, int32_t *phy2log,
                        int32_t *phy_quota, int32_t *logcnt, int32_t *log2phy, int32_t *steps,
-                       uint32_t *status, hipStream_t s, int spr) {
+                       uint32_t *status, hipStream_t s, int cfg) {
     PlanArgs a{L.num_experts, L.num_ranks, L.num_phys, L.num_spare, L.max_replicas, tables_of(L)};
     const dim3 g((unsigned)P), b(kWave);
     const size_t lds = lanes_lds_bytes(L);
-    switch (spr) {
-        case 1: hipLaunchKernelGGL(plan_kernel_lanes<1>, g, b, lds, s, load, a, phy2log, phy_quota, logcnt, log2phy, steps, status); break;
-        case 2: hipLaunchKernelGGL(plan_kernel_lanes<2>, g, b, lds, s, load, a, phy2log, phy_quota, logcnt, log2phy, steps, status); break;
-        case 4: hipLaunchKernelGGL(plan_kernel_lanes<4>, g, b, lds, s, load, a, phy2log, phy_quota, logcnt, log2phy, steps, status); break;
-        case 8: hipLaunchKernelGGL(plan_kernel_lanes<8>, g, b, lds, s, load, a, phy2log, phy_quota, logcnt, log2phy, steps, status); break;
-        case 16: hipLaunchKernelGGL(plan_kernel_lanes<16>, g, b, lds, s, load, a, phy2log, phy_quota, logcnt, log2phy, steps, status); break;
+    switch (cfg) {
+        EP_LANES_ROW(1)
+        EP_LANES_ROW(2)
+        EP_LANES_ROW(4)
+        EP_LANES_ROW(8)
         default:
             hipLaunchKernelGGL(plan_kernel_generic, g, b, plan_lds_bytes(L), s, load, a, phy2log,
                                phy_quota, logcnt, log2phy, steps, status);
