@@ -49,6 +49,8 @@ def lib() -> ctypes.CDLL:
         _lib.or_layout.restype = ctypes.c_int
         _lib.or_waterfill.argtypes = [i64, i32, i64p, i32p, i64p]
         _lib.or_waterfill.restype = ctypes.c_int
+        _lib.or_dispatch.argtypes = [i32p, i64, i32, i32, i32p, i32p, i32p, i32, i64p, i32p, i32p]
+        _lib.or_dispatch.restype = ctypes.c_int64
     return _lib
 
 
@@ -200,6 +202,20 @@ def waterfill(T: int, backgrounds, ranks) -> np.ndarray:
     q = np.zeros(b.size, np.int64)
     lib().or_waterfill(int(T), b.size, b, r, q)
     return q
+
+
+def dispatch(ids: np.ndarray, num_experts: int, phy_quota, log2phy, logcnt):
+    """Dispatch layout of one plan: (slot_off[Phi+1], pos[N], src[N], placed pairs)."""
+    ids = _i32(ids).reshape(-1)
+    log2phy = _i32(log2phy)
+    rho = log2phy.shape[-1]
+    q = _i32(phy_quota)
+    off = np.zeros(q.size + 1, np.int64)
+    pos = np.zeros(max(ids.size, 1), np.int32)
+    src = np.zeros(max(ids.size, 1), np.int32)
+    placed = lib().or_dispatch(ids, ids.size, num_experts, q.size, q, log2phy.reshape(-1), _i32(logcnt),
+                               rho, off, pos, src)
+    return off, pos[: ids.size], src[: ids.size], int(placed)
 
 
 def run_path(ids_2d: np.ndarray, layout: Layout):

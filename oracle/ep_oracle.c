@@ -414,3 +414,44 @@ int or_waterfill(int64_t T, int32_t n, const int64_t *b, const int32_t *rank, in
     free(rk);
     return OR_OK;
 }
+
+/* ------------------------------------------------------------------------- */
+/* Next row: dispatch layout for the token all-to-all [EPLB tutorial, EPLB / */
+/* DeepEP section: dispatch sends each pair to its physical replica, combine */
+/* gathers the results back to the logical expert].  Pairs are laid out     */
+/* physical-slot-major: slot s owns positions [off_s, off_s + quota_s) with   */
+/* off the exclusive prefix of the quotas in slot order, and the j-th pair of */
+/* expert e, served by instance s whose range starts at Q, sits at           */
+/* off_s + (j - Q).  pos[p] is that position (-1 for padding, invalid IDs    */
+/* and pairs past the expert's quotas); src[k] is the pair at position k     */
+/* (-1 where no pair lands).  Returns the number of placed pairs.            */
+/* ------------------------------------------------------------------------- */
+int64_t or_dispatch(const int32_t *ids, int64_t n, int32_t E, int32_t Phi, const int32_t *phy_quota,
+                    const int32_t *log2phy, const int32_t *logcnt, int32_t rho,
+                    int64_t *slot_off, int32_t *pos, int32_t *src) {
+    slot_off[0] = 0;
+    for (int s = 0; s < Phi; s++) slot_off[s + 1] = slot_off[s] + phy_quota[s];
+    for (int64_t k = 0; k < n; k++) src[k] = -1;
+    int64_t *seen = calloc((size_t)E, sizeof(int64_t));
+    int64_t placed = 0;
+    for (int64_t p = 0; p < n; p++) {
+        int32_t v = ids[p];
+        pos[p] = -1;
+        if (v < 0 || v >= E) continue;
+        int64_t j = seen[v]++;
+        int64_t Q = 0;
+        for (int t = 0; t < logcnt[v] && t < rho; t++) {
+            int32_t s = log2phy[(int64_t)v * rho + t];
+            if (j < Q + phy_quota[s]) {
+                int64_t k = slot_off[s] + (j - Q);
+                pos[p] = (int32_t)k;
+                if (k < n) src[k] = (int32_t)p;
+                placed++;
+                break;
+            }
+            Q += phy_quota[s];
+        }
+    }
+    free(seen);
+    return placed;
+}
