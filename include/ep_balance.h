@@ -178,6 +178,28 @@ int ep_reroute(const int32_t *topk_ids, int64_t pairs_per_plan, int32_t num_plan
                ep_stream_t stream);
 
 /*
+ * Next row after A3 -- dispatch layout for the token all-to-all (EPLB
+ * tutorial, EPLB / DeepEP section: dispatch sends each pair to its physical
+ * replica; combine gathers results back to the logical expert).  Pairs are
+ * laid out physical-slot-major: slot s owns positions [off_s, off_s + quota_s)
+ * with off the exclusive prefix of the quotas in slot order, and the j-th pair
+ * of expert e, served by the instance whose quota range starts at Q, sits at
+ * off_s + (j - Q): for plans whose quotas cover the loads, the stable counting
+ * sort of the pairs by physical slot.
+ *   topk_ids, plan tables, ws  as for ep_reroute (the same histogram workspace)
+ *   slot_offsets  device int32 [P][Phi+1] (written): off_s, last entry = total
+ *   dispatch_pos  device int32 [P][N] (written): position of each pair, -1 for
+ *                 padding, invalid IDs and pairs past the expert's quotas
+ *   dispatch_src  device int32 [P][N] (written): pair index (within the plan)
+ *                 at each position, -1 for positions no pair takes
+ */
+int ep_dispatch_layout(const int32_t *topk_ids, int64_t pairs_per_plan, int32_t num_plans,
+                       const ep_layout_t *layout, const int32_t *phy_quota, const int32_t *log2phy,
+                       const int32_t *logcnt, const void *ws, size_t ws_bytes,
+                       int32_t *slot_offsets, int32_t *dispatch_pos, int32_t *dispatch_src,
+                       ep_stream_t stream);
+
+/*
  * A4 -- weight distribution on one GPU: gather the weights of every expert that
  * occupies a spare slot into that slot's row of the cross-layer slot buffer
  * (UltraEP article, key designs: reserved slots, weight buffers reused across

@@ -63,11 +63,12 @@ def lib() -> ctypes.CDLL:
         L.ep_plan_quota.argtypes = [vp, i32, lp, vp, vp, vp, vp, vp, vp, vp]
         L.ep_reroute.argtypes = [vp, i64, i32, lp, vp, vp, vp, vp, sz, vp, vp]
         L.ep_slot_fill.argtypes = [vp, i64, vp, lp, vp, vp]
+        L.ep_dispatch_layout.argtypes = [vp, i64, i32, lp, vp, vp, vp, vp, sz, vp, vp, vp, vp]
         L.ep_balance_stats.argtypes = [vp, vp, i32, lp, vp, vp, vp, vp]
         L.ep_status_string.argtypes = [ctypes.c_int]
         L.ep_status_string.restype = ctypes.c_char_p
         for f in ("ep_layout_init", "ep_load_histogram", "ep_plan_quota", "ep_reroute",
-                  "ep_slot_fill", "ep_balance_stats"):
+                  "ep_slot_fill", "ep_balance_stats", "ep_dispatch_layout"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -205,6 +206,27 @@ def ep_reroute(topk_ids: torch.Tensor, layout: Layout, phy_quota: torch.Tensor, 
                           _stream(stream))
     _check(rc, "ep_reroute")
     return phys_ids
+
+
+def ep_dispatch_layout(topk_ids: torch.Tensor, layout: Layout, phy_quota: torch.Tensor,
+                       log2phy: torch.Tensor, logcnt: torch.Tensor, ws: torch.Tensor, slot_offsets=None,
+                       dispatch_pos=None, dispatch_src=None, stream=None):
+    """-> (slot_offsets int32 [P][Phi+1], dispatch_pos int32 [P][N], dispatch_src int32 [P][N])."""
+    _dev(topk_ids, torch.int32, "topk_ids")
+    for t, n in ((phy_quota, "phy_quota"), (log2phy, "log2phy"), (logcnt, "logcnt")):
+        _dev(t, torch.int32, n)
+    P, N = topk_ids.shape
+    dev = topk_ids.device
+    if slot_offsets is None:
+        slot_offsets = torch.empty((P, layout.num_phys + 1), dtype=torch.int32, device=dev)
+    dispatch_pos = torch.empty_like(topk_ids) if dispatch_pos is None else dispatch_pos
+    dispatch_src = torch.empty_like(topk_ids) if dispatch_src is None else dispatch_src
+    rc = lib().ep_dispatch_layout(_ptr(topk_ids), N, P, layout.ref(), _ptr(phy_quota), _ptr(log2phy),
+                                  _ptr(logcnt), _ptr(ws), ws.numel() * ws.element_size(),
+                                  _ptr(slot_offsets), _ptr(dispatch_pos), _ptr(dispatch_src),
+                                  _stream(stream))
+    _check(rc, "ep_dispatch_layout")
+    return slot_offsets, dispatch_pos, dispatch_src
 
 
 def ep_slot_fill(expert_weights: torch.Tensor, phy2log: torch.Tensor, layout: Layout,

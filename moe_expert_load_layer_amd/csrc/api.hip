@@ -165,6 +165,24 @@ int ep_reroute(const int32_t *topk_ids, int64_t N, int32_t P, const ep_layout_t 
                                  phys_ids, as_stream(stream)));
 }
 
+int ep_dispatch_layout(const int32_t *topk_ids, int64_t N, int32_t P, const ep_layout_t *layout,
+                       const int32_t *phy_quota, const int32_t *log2phy, const int32_t *logcnt,
+                       const void *ws, size_t ws_size, int32_t *slot_offsets, int32_t *dispatch_pos,
+                       int32_t *dispatch_src, ep_stream_t stream) {
+    if (!layout_ok(layout) || !pairs_ok(topk_ids, N, P) || !phy_quota || !log2phy || !logcnt ||
+        !slot_offsets)
+        return EP_ERR_INVALID_ARG;
+    if (N > 0 && (!dispatch_pos || !dispatch_src)) return EP_ERR_INVALID_ARG;
+    const int E = layout->num_experts;
+    if (dispatch_lds_bytes(E, layout->num_phys, 1) > kMaxLds) return EP_ERR_INVALID_ARG;
+    const size_t need = ws_bytes(N, P, E);
+    if (ws_size < need || (need > 0 && (!ws || !aligned(ws, 16)))) return EP_ERR_INVALID_ARG;
+    const int64_t sub = sub_pairs(N, P, E);
+    return hip_rc(launch_dispatch(topk_ids, N, P, *layout, sub, num_sub(N, sub),
+                                  static_cast<const int32_t *>(ws), phy_quota, log2phy, logcnt,
+                                  slot_offsets, dispatch_pos, dispatch_src, as_stream(stream)));
+}
+
 int ep_slot_fill(const void *expert_weights, int64_t bytes_per_expert, const int32_t *phy2log,
                  const ep_layout_t *layout, void *slot_buf, ep_stream_t stream) {
     if (!layout_ok(layout) || !phy2log || bytes_per_expert <= 0 || bytes_per_expert % 16 != 0)

@@ -198,6 +198,11 @@ hipError_t launch_reroute(const int32_t *ids, int64_t N, int32_t P, const ep_lay
                           const int32_t *log2phy, const int32_t *logcnt, int32_t *out,
                           hipStream_t s);
 size_t reroute_lds_bytes(int E, int Phi, int waves);
+hipError_t launch_dispatch(const int32_t *ids, int64_t N, int32_t P, const ep_layout_t &L, int64_t sub,
+                           int64_t nsb, const int32_t *ws, const int32_t *phy_quota,
+                           const int32_t *log2phy, const int32_t *logcnt, int32_t *slot_offsets,
+                           int32_t *dpos, int32_t *dsrc, hipStream_t s);
+size_t dispatch_lds_bytes(int E, int Phi, int waves);
 hipError_t launch_slot_fill(const void *w, int64_t bytes_per_expert, const int32_t *phy2log,
                             const ep_layout_t &L, void *buf, hipStream_t s);
 hipError_t launch_stats(const int32_t *load, const int32_t *phy_quota, int32_t P,
