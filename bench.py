@@ -203,6 +203,16 @@ def main(argv=None) -> int:
     lat_rr = lat(lambda: ep.ep_reroute(ids1, lay, pl1.phy_quota, pl1.log2phy, pl1.logcnt, ws1, phys_ids=ph1),
                  args.latency_reps)
 
+    # next rows beyond the timed step, one launch over all plans each
+    slot_off = torch.empty((P, lay.num_phys + 1), dtype=torch.int32, device=dev)
+    dpos = torch.empty_like(ids)
+    dsrc = torch.empty_like(ids)
+    disp_ms = lat(lambda: ep.ep_dispatch_layout(ids, lay, plan.phy_quota, plan.log2phy, plan.logcnt, ws,
+                                                slot_offsets=slot_off, dispatch_pos=dpos,
+                                                dispatch_src=dsrc), 5) * 1e-3
+    next_rows = {"dispatch_layout_ms": disp_ms,
+                 "dispatch_layout_GBps": 12.0 * P * N / (disp_ms * 1e-3) / 1e9}
+
     traffic = None
     if TRAFFIC and TRAFFIC.get("kernel_sha") == _src_sha("slotfill.hip"):
         traffic = TRAFFIC["bytes_per_launch"]
@@ -239,6 +249,7 @@ def main(argv=None) -> int:
             "hist_us_single_layer": lat_hist,
             "reroute_us_single_layer": lat_rr,
         },
+        "next_rows": next_rows,
         "balance": {
             "imbalance_before_mean": float(imb_np[:, 0].mean()),
             "imbalance_after_mean": float(imb_np[:, 1].mean()),

@@ -51,6 +51,9 @@ def lib() -> ctypes.CDLL:
         _lib.or_waterfill.restype = ctypes.c_int
         _lib.or_dispatch.argtypes = [i32p, i64, i32, i32, i32p, i32p, i32p, i32, i64p, i32p, i32p]
         _lib.or_dispatch.restype = ctypes.c_int64
+        f32p = np.ctypeslib.ndpointer(np.float32, flags="C_CONTIGUOUS")
+        _lib.or_grad_reduce.argtypes = [f32p, i64, f32p, i32, i32, i32p, i32p, i32p, i32p, i32p, i32]
+        _lib.or_grad_reduce.restype = ctypes.c_int
     return _lib
 
 
@@ -216,6 +219,20 @@ def dispatch(ids: np.ndarray, num_experts: int, phy_quota, log2phy, logcnt):
     placed = lib().or_dispatch(ids, ids.size, num_experts, q.size, q, log2phy.reshape(-1), _i32(logcnt),
                                rho, off, pos, src)
     return off, pos[: ids.size], src[: ids.size], int(placed)
+
+
+def grad_reduce(native_grads: np.ndarray, slot_grads: np.ndarray, layout: Layout, log2phy, logcnt):
+    """In place: every replicated expert's row of native_grads becomes the fp32
+    fold of its instances' rows in ascending slot order."""
+    assert native_grads.dtype == np.float32 and native_grads.flags["C_CONTIGUOUS"]
+    n = native_grads.shape[1]
+    sg = np.ascontiguousarray(slot_grads, dtype=np.float32).reshape(-1)
+    l2p = _i32(log2phy)
+    rc = lib().or_grad_reduce(native_grads.reshape(-1), n, sg if sg.size else np.zeros(1, np.float32),
+                              *layout.args(), l2p.reshape(-1), _i32(logcnt), l2p.shape[-1])
+    if rc != 0:
+        raise ValueError(f"oracle: bad layout ({rc})")
+    return native_grads
 
 
 def run_path(ids_2d: np.ndarray, layout: Layout):

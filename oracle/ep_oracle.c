@@ -455,3 +455,46 @@ int64_t or_dispatch(const int32_t *ids, int64_t n, int32_t E, int32_t Phi, const
     free(seen);
     return placed;
 }
+
+/* ------------------------------------------------------------------------- */
+/* Next row: replica gradient reduction [UltraEP article, key designs:       */
+/* replicas keep no optimizer state and their gradients are reduced back to  */
+/* the native expert during backward; the backward paragraph: accumulation   */
+/* keeps a fixed order so the reduction is deterministic].  For every expert */
+/* with replicas, its gradient becomes the fp32 fold of its instances'       */
+/* gradients in ascending physical-slot order:                               */
+/*     acc = g(inst 0); acc = acc + g(inst 1); ...                            */
+/* where the native instance reads native_grads[e] and a replica in spare    */
+/* slot o reads slot_grads[o].  The result overwrites native_grads[e].       */
+/* ------------------------------------------------------------------------- */
+int or_grad_reduce(float *native_grads, int64_t n, const float *slot_grads, int32_t E, int32_t R,
+                   const int32_t *native_count, const int32_t *native_experts,
+                   const int32_t *spare_count, const int32_t *log2phy, const int32_t *logcnt,
+                   int32_t rho) {
+    layout_t L;
+    int rc = layout_build(&L, E, R, native_count, native_experts, spare_count);
+    if (rc != OR_OK) return rc;
+    int *spare_of = malloc((size_t)L.Phi * sizeof(int));
+    for (int s = 0; s < L.Phi; s++) spare_of[s] = -1;
+    for (int o = 0; o < L.S; o++) spare_of[L.spare_slot[o]] = o;
+    for (int e = 0; e < E; e++) {
+        int c = logcnt[e] < rho ? logcnt[e] : rho;
+        if (c < 2) continue;
+        const float **rows = malloc((size_t)c * sizeof(float *));
+        for (int t = 0; t < c; t++) {
+            int s = log2phy[(int64_t)e * rho + t];
+            rows[t] = L.slot_home[s] >= 0 ? native_grads + (int64_t)L.slot_home[s] * n
+                                          : slot_grads + (int64_t)spare_of[s] * n;
+        }
+        float *out = native_grads + (int64_t)e * n;
+        for (int64_t k = 0; k < n; k++) {
+            float acc = rows[0][k];
+            for (int t = 1; t < c; t++) acc = acc + rows[t][k];
+            out[k] = acc;
+        }
+        free(rows);
+    }
+    free(spare_of);
+    layout_free(&L);
+    return OR_OK;
+}
