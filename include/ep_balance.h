@@ -213,6 +213,25 @@ int ep_slot_fill(const void *expert_weights, int64_t bytes_per_expert, const int
                  const ep_layout_t *layout, void *slot_buf, ep_stream_t stream);
 
 /*
+ * Next row -- replica gradient reduction in backward (UltraEP article, key
+ * designs: replicas keep no optimizer state and their gradients are reduced
+ * back to the native expert; backward paragraph: accumulation keeps a fixed
+ * order so the reduction is deterministic).  One plan (one layer) per call:
+ * for every expert with logcnt >= 2, its native row becomes the fp32 fold of
+ * its instances' gradient rows in ascending physical-slot order
+ *     acc = g(inst 0); acc = acc + g(inst 1); ...
+ * reading native_grads[e] for the native instance and slot_grads[o] for the
+ * replica in the o-th spare slot.  Other rows and slot_grads are not written.
+ *   native_grads device float [E][n] (in/out), 16-byte aligned
+ *   slot_grads   device float [S][n], the gradient half of the slot buffer
+ *   log2phy, logcnt  that layer's plan (ep_plan_quota)
+ * n = elems_per_expert must be a positive multiple of 4.
+ */
+int ep_replica_grad_reduce(float *native_grads, int64_t elems_per_expert, const float *slot_grads,
+                           const int32_t *log2phy, const int32_t *logcnt, const ep_layout_t *layout,
+                           ep_stream_t stream);
+
+/*
  * A5 -- balance statistics per plan (UltraEP digest, "Reported results":
  * most loaded rank over the mean).
  *   stats      device int64 [P][4]: max rank load before (native placement),

@@ -64,11 +64,12 @@ def lib() -> ctypes.CDLL:
         L.ep_reroute.argtypes = [vp, i64, i32, lp, vp, vp, vp, vp, sz, vp, vp]
         L.ep_slot_fill.argtypes = [vp, i64, vp, lp, vp, vp]
         L.ep_dispatch_layout.argtypes = [vp, i64, i32, lp, vp, vp, vp, vp, sz, vp, vp, vp, vp]
+        L.ep_replica_grad_reduce.argtypes = [vp, i64, vp, vp, vp, lp, vp]
         L.ep_balance_stats.argtypes = [vp, vp, i32, lp, vp, vp, vp, vp]
         L.ep_status_string.argtypes = [ctypes.c_int]
         L.ep_status_string.restype = ctypes.c_char_p
         for f in ("ep_layout_init", "ep_load_histogram", "ep_plan_quota", "ep_reroute",
-                  "ep_slot_fill", "ep_balance_stats", "ep_dispatch_layout"):
+                  "ep_slot_fill", "ep_balance_stats", "ep_dispatch_layout", "ep_replica_grad_reduce"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -227,6 +228,20 @@ def ep_dispatch_layout(topk_ids: torch.Tensor, layout: Layout, phy_quota: torch.
                                   _stream(stream))
     _check(rc, "ep_dispatch_layout")
     return slot_offsets, dispatch_pos, dispatch_src
+
+
+def ep_replica_grad_reduce(native_grads: torch.Tensor, slot_grads: torch.Tensor, log2phy: torch.Tensor,
+                           logcnt: torch.Tensor, layout: Layout, stream=None) -> torch.Tensor:
+    """native_grads float32 [E][n] (in place), slot_grads float32 [S][n], one plan's log2phy/logcnt."""
+    _dev(native_grads, torch.float32, "native_grads")
+    _dev(log2phy, torch.int32, "log2phy"); _dev(logcnt, torch.int32, "logcnt")
+    if layout.num_spare:
+        _dev(slot_grads, torch.float32, "slot_grads")
+    n = native_grads.shape[1]
+    rc = lib().ep_replica_grad_reduce(_ptr(native_grads), n, _ptr(slot_grads) if layout.num_spare else None,
+                                      _ptr(log2phy), _ptr(logcnt), layout.ref(), _stream(stream))
+    _check(rc, "ep_replica_grad_reduce")
+    return native_grads
 
 
 def ep_slot_fill(expert_weights: torch.Tensor, phy2log: torch.Tensor, layout: Layout,

@@ -75,6 +75,7 @@ int ep_layout_init(int32_t E, int32_t R, const int32_t *native_count, const int3
     int32_t *slot_rank = slot_home + Phi;
     int32_t *home_slot = slot_rank + Phi;
     int32_t *spare_slot = home_slot + E;
+    int32_t *slot_spare = spare_slot + S;
     for (int e = 0; e < E; e++) home_slot[e] = -1;
     int slot = 0, in = 0, o = 0;
     std::vector<int32_t> blk;
@@ -96,11 +97,13 @@ int ep_layout_init(int32_t E, int32_t R, const int32_t *native_count, const int3
             home_slot[e] = slot;
             slot_home[slot] = e;
             slot_rank[slot] = r;
+            slot_spare[slot] = -1;
             slot++;
         }
         for (int i = 0; i < spare_count[r]; i++) {
             slot_home[slot] = -1;
             slot_rank[slot] = r;
+            slot_spare[slot] = o;
             spare_slot[o++] = slot;
             slot++;
         }
@@ -181,6 +184,18 @@ int ep_dispatch_layout(const int32_t *topk_ids, int64_t N, int32_t P, const ep_l
     return hip_rc(launch_dispatch(topk_ids, N, P, *layout, sub, num_sub(N, sub),
                                   static_cast<const int32_t *>(ws), phy_quota, log2phy, logcnt,
                                   slot_offsets, dispatch_pos, dispatch_src, as_stream(stream)));
+}
+
+int ep_replica_grad_reduce(float *native_grads, int64_t elems_per_expert, const float *slot_grads,
+                           const int32_t *log2phy, const int32_t *logcnt, const ep_layout_t *layout,
+                           ep_stream_t stream) {
+    if (!layout_ok(layout) || !log2phy || !logcnt || elems_per_expert <= 0 || elems_per_expert % 4 != 0)
+        return EP_ERR_INVALID_ARG;
+    if (!native_grads || !aligned(native_grads, 16)) return EP_ERR_INVALID_ARG;
+    if (layout->num_spare > 0 && (!slot_grads || !aligned(slot_grads, 16))) return EP_ERR_INVALID_ARG;
+    if (layout->num_experts > kMaxPlans) return EP_ERR_INVALID_ARG;
+    return hip_rc(launch_grad_reduce(native_grads, elems_per_expert, slot_grads, log2phy, logcnt, *layout,
+                                     as_stream(stream)));
 }
 
 int ep_slot_fill(const void *expert_weights, int64_t bytes_per_expert, const int32_t *phy2log,

@@ -22,13 +22,14 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 //   slot_rank  [Phi]  rank owning a slot
 //   home_slot  [E]    native slot of each expert
 //   spare_slot [S]    physical slot of the o-th spare slot (ascending)
+//   slot_spare [Phi]  spare ordinal of a slot, -1 for a native slot
 // ---------------------------------------------------------------------------
 struct Tables {
-    const int32_t *rank_first, *rank_nat, *slot_home, *slot_rank, *home_slot, *spare_slot;
+    const int32_t *rank_first, *rank_nat, *slot_home, *slot_rank, *home_slot, *spare_slot, *slot_spare;
 };
 
 inline size_t table_ints(int E, int R, int S) {
-    return (size_t)(2 * R + 1) + 2 * (size_t)(E + S) + (size_t)E + (size_t)S;
+    return (size_t)(2 * R + 1) + 3 * (size_t)(E + S) + (size_t)E + (size_t)S;
 }
 
 inline Tables tables_of(const ep_layout_t &L) {
@@ -40,6 +41,7 @@ inline Tables tables_of(const ep_layout_t &L) {
     t.slot_rank = t.slot_home + Phi;
     t.home_slot = t.slot_rank + Phi;
     t.spare_slot = t.home_slot + E;
+    t.slot_spare = t.spare_slot + L.num_spare;
     return t;
 }
 
@@ -203,6 +205,8 @@ hipError_t launch_dispatch(const int32_t *ids, int64_t N, int32_t P, const ep_la
                            const int32_t *log2phy, const int32_t *logcnt, int32_t *slot_offsets,
                            int32_t *dpos, int32_t *dsrc, hipStream_t s);
 size_t dispatch_lds_bytes(int E, int Phi, int waves);
+hipError_t launch_grad_reduce(float *native, int64_t n, const float *slot, const int32_t *log2phy,
+                              const int32_t *logcnt, const ep_layout_t &L, hipStream_t s);
 hipError_t launch_slot_fill(const void *w, int64_t bytes_per_expert, const int32_t *phy2log,
                             const ep_layout_t &L, void *buf, hipStream_t s);
 hipError_t launch_stats(const int32_t *load, const int32_t *phy_quota, int32_t P,

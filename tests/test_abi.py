@@ -20,7 +20,8 @@ def _declared():
 def test_header_declares_the_path():
     names = _declared()
     for n in ("ep_load_histogram", "ep_plan_quota", "ep_reroute", "ep_slot_fill", "ep_balance_stats",
-              "ep_workspace_bytes", "ep_layout_init", "ep_layout_table_ints", "ep_status_string"):
+              "ep_workspace_bytes", "ep_layout_init", "ep_layout_table_ints", "ep_status_string",
+              "ep_dispatch_layout", "ep_replica_grad_reduce"):
         assert n in names
 
 
@@ -40,7 +41,7 @@ def test_host_side_checks_without_gpu():
     L = ep.lib()
     assert L.ep_status_string(0) == b"EP_OK"
     assert L.ep_status_string(-1) == b"EP_ERR_INVALID_ARG"
-    assert L.ep_layout_table_ints(12, 8, 4) == 2 * 8 + 1 + 2 * 16 + 12 + 4
+    assert L.ep_layout_table_ints(12, 8, 4) == 2 * 8 + 1 + 3 * 16 + 12 + 4
     assert L.ep_workspace_bytes(-1, 1, 4) == 0
     assert L.ep_workspace_bytes(0, 3, 4) == 3 * 1 * 5 * 4      # only the per-plan totals row
     # workspace grows with the number of sub-blocks
