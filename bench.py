@@ -212,6 +212,18 @@ def main(argv=None) -> int:
                                                 dispatch_src=dsrc), 5) * 1e-3
     next_rows = {"dispatch_layout_ms": disp_ms,
                  "dispatch_layout_GBps": 12.0 * P * N / (disp_ms * 1e-3) / 1e9}
+    # backward: fold replica gradients (fp32, 3x4096x1536 per expert) into the
+    # native rows for layer 0's plan
+    n_el = bpe // 2
+    g_native = torch.zeros((E, n_el), dtype=torch.float32, device=dev)
+    g_slot = torch.zeros((S, n_el), dtype=torch.float32, device=dev)
+    l2p0, lc0 = plan.log2phy[0].contiguous(), plan.logcnt[0].contiguous()
+    red_ms = lat(lambda: ep.ep_replica_grad_reduce(g_native, g_slot, l2p0, lc0, lay), 5) * 1e-3
+    lc_h = lc0.cpu().numpy()
+    red_bytes = float(((lc_h + 1) * (lc_h >= 2)).sum()) * n_el * 4
+    next_rows.update({"grad_reduce_ms": red_ms, "grad_reduce_bytes": red_bytes,
+                      "grad_reduce_GBps": red_bytes / (red_ms * 1e-3) / 1e9})
+    del g_native, g_slot
 
     traffic = None
     if TRAFFIC and TRAFFIC.get("kernel_sha") == _src_sha("slotfill.hip"):

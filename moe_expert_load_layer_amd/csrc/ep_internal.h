@@ -57,7 +57,7 @@ inline Tables tables_of(const ep_layout_t &L) {
 #define EP_SUB_TARGET_WAVES 8192
 #endif
 #ifndef EP_SUB_MAX
-#define EP_SUB_MAX 8192
+#define EP_SUB_MAX 4096
 #endif
 #ifndef EP_SUB_MIN
 #define EP_SUB_MIN 2048
@@ -204,7 +204,7 @@ hipError_t launch_dispatch(const int32_t *ids, int64_t N, int32_t P, const ep_la
                            int64_t nsb, const int32_t *ws, const int32_t *phy_quota,
                            const int32_t *log2phy, const int32_t *logcnt, int32_t *slot_offsets,
                            int32_t *dpos, int32_t *dsrc, hipStream_t s);
-size_t dispatch_lds_bytes(int E, int Phi, int waves);
+size_t dispatch_lds_bytes(int E, int Phi, int waves, int64_t stage_pairs);
 hipError_t launch_grad_reduce(float *native, int64_t n, const float *slot, const int32_t *log2phy,
                               const int32_t *logcnt, const ep_layout_t &L, hipStream_t s);
 hipError_t launch_slot_fill(const void *w, int64_t bytes_per_expert, const int32_t *phy2log,
