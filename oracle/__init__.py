@@ -39,6 +39,9 @@ def lib() -> ctypes.CDLL:
         _lib.or_plan.argtypes = [i32, i32, i32p, i32p, i32p, i32p, i32p, i32p, i32p, i32p, i32,
                                  ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
         _lib.or_plan.restype = ctypes.c_int
+        _lib.or_plan_domain.argtypes = [i32, i32, i32p, i32p, i32p, i32p, i32p, i32p, i32p, i32p, i32, i32,
+                                        ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
+        _lib.or_plan_domain.restype = ctypes.c_int
         _lib.or_reroute.argtypes = [i32p, i64, i32, i32p, i32p, i32p, i32, i32p]
         _lib.or_reroute.restype = ctypes.c_int64
         _lib.or_slot_fill.argtypes = [u8p, i64, i32, i32, i32p, i32p, i32p, i32p, u8p]
@@ -126,7 +129,8 @@ class Plan:
     cap_hit: int
 
 
-def plan(load: np.ndarray, layout: Layout) -> Plan:
+def plan(load: np.ndarray, layout: Layout, ranks_per_domain: int = 0) -> Plan:
+    """ranks_per_domain > 0 keeps every replica in its native rank's domain (rank // D)."""
     E, Phi, rho = layout.num_experts, layout.num_phys, layout.max_replicas
     load = _i32(load).reshape(-1)
     assert load.size == E
@@ -136,8 +140,8 @@ def plan(load: np.ndarray, layout: Layout) -> Plan:
     log2phy = np.zeros(E * rho, np.int32)
     steps = ctypes.c_int32(0)
     cap = ctypes.c_int32(0)
-    rc = lib().or_plan(*layout.args(), load, phy2log, quota, logcnt, log2phy, rho,
-                       ctypes.byref(steps), ctypes.byref(cap))
+    rc = lib().or_plan_domain(*layout.args(), load, phy2log, quota, logcnt, log2phy, rho,
+                              int(ranks_per_domain), ctypes.byref(steps), ctypes.byref(cap))
     if rc != 0:
         raise ValueError(f"oracle: bad layout ({rc})")
     return Plan(phy2log, quota, logcnt, log2phy.reshape(E, rho), int(steps.value), int(cap.value))

@@ -48,7 +48,7 @@ def _popcount_vec(x: np.ndarray) -> np.ndarray:
 
 
 def brute_force_optimum(load: Sequence[int], num_ranks: int, native_rank: Sequence[int],
-                        spare_count: Sequence[int]) -> int:
+                        spare_count: Sequence[int], ranks_per_domain: int = 0) -> int:
     """Exact minimum of the max rank load over every use of the spare slots.
 
     ``native_rank[e]`` is the rank hosting expert e's native instance.  A spare
@@ -70,7 +70,8 @@ def brute_force_optimum(load: Sequence[int], num_ranks: int, native_rank: Sequen
     # choices per rank: tuples of distinct experts not native on r (order-free), size <= spare
     per_rank = []
     for r in range(R):
-        pool = [e for e in range(E) if e not in hosted[r]]
+        pool = [e for e in range(E) if e not in hosted[r] and
+                (ranks_per_domain <= 0 or r // ranks_per_domain == int(native_rank[e]) // ranks_per_domain)]
         opts = []
         for k in range(0, int(spare_count[r]) + 1):
             opts.extend(itertools.combinations(pool, k))

@@ -184,10 +184,14 @@ static void waterfill(int64_t T, int n, const int64_t *b, const int *rank, int64
 /* ------------------------------------------------------------------------- */
 typedef struct { int slot; int expert; int64_t quota; } cand_t;
 
-int or_plan(int32_t E, int32_t R, const int32_t *native_count, const int32_t *native_experts,
-            const int32_t *spare_count, const int32_t *load,
-            int32_t *phy2log, int32_t *phy_quota, int32_t *logcnt, int32_t *log2phy,
-            int32_t rho, int32_t *steps_out, int32_t *cap_hit_out) {
+/* ranks_per_domain D > 0 confines replicas to the scale-up domain of the
+ * expert's native rank (rank r lies in domain r / D) [UltraEP article, section
+ * on why it reaches the optimum: hot-expert replication stays inside the
+ * high-bandwidth scale-up domain]; D = 0 places replicas anywhere. */
+int or_plan_domain(int32_t E, int32_t R, const int32_t *native_count, const int32_t *native_experts,
+                   const int32_t *spare_count, const int32_t *load,
+                   int32_t *phy2log, int32_t *phy_quota, int32_t *logcnt, int32_t *log2phy,
+                   int32_t rho, int32_t ranks_per_domain, int32_t *steps_out, int32_t *cap_hit_out) {
     layout_t L;
     int rc = layout_build(&L, E, R, native_count, native_experts, spare_count);
     if (rc != OR_OK) return rc;
@@ -263,8 +267,10 @@ int or_plan(int32_t E, int32_t R, const int32_t *native_count, const int32_t *na
                 n++;
             }
             int d = -1;
+            const int home_rank = L.slot_rank[L.home_slot[e]];
             for (int r = 0; r < R; r++) {
                 if (freec[r] <= 0) continue;
+                if (ranks_per_domain > 0 && r / ranks_per_domain != home_rank / ranks_per_domain) continue;
                 int hosts = 0;
                 for (int i = 0; i < n; i++) if (ir[i] == r) hosts = 1;
                 if (hosts) continue;
@@ -307,6 +313,14 @@ int or_plan(int32_t E, int32_t R, const int32_t *native_count, const int32_t *na
     free(ir); free(is); free(ib); free(iq); free(nq);
     layout_free(&L);
     return OR_OK;
+}
+
+int or_plan(int32_t E, int32_t R, const int32_t *native_count, const int32_t *native_experts,
+            const int32_t *spare_count, const int32_t *load,
+            int32_t *phy2log, int32_t *phy_quota, int32_t *logcnt, int32_t *log2phy,
+            int32_t rho, int32_t *steps_out, int32_t *cap_hit_out) {
+    return or_plan_domain(E, R, native_count, native_experts, spare_count, load, phy2log, phy_quota,
+                          logcnt, log2phy, rho, 0, steps_out, cap_hit_out);
 }
 
 /* ------------------------------------------------------------------------- */
