@@ -81,6 +81,10 @@ typedef struct ep_layout {
     int32_t max_replicas; /* rho = min(R, 1 + S): row width of log2phy            */
     int32_t max_rank_natives; /* most native experts on one rank                  */
     int32_t max_rank_spares;  /* most spare slots on one rank                     */
+    int32_t ranks_per_domain; /* D > 0: replicas stay in the scale-up domain of     */
+                              /* their expert's native rank (rank r is in domain    */
+                              /* r / D; an 8-GPU xGMI node on MI355X); 0: anywhere. */
+                              /* ep_layout_init sets 0; the caller may change it.   */
     const int32_t *tables;/* device, packed tables (see ep_layout_init)           */
 } ep_layout_t;
 
@@ -143,6 +147,9 @@ int ep_load_histogram(const int32_t *topk_ids, int64_t pairs_per_plan, int32_t n
  *   over its instances: with other-expert loads b_i sorted by (b, rank), the m*
  *   largest-prefix instances with m*b_(m) < load + sum_{j<=m} b_(j) end at
  *   floor(S/m*) or one more (the extra units to the first S mod m* of them).
+ *   With layout->ranks_per_domain = D > 0 the replica rank must also share the
+ *   expert's native domain (UltraEP article, section on why it reaches the
+ *   optimum: replication stays inside the high-bandwidth scale-up domain).
  *   A move is kept only if it lowers h's load; the loop stops when no move
  *   does.  Replicas left with quota 0 are freed.
  *   load      device int32 [P][E]

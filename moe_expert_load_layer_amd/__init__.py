@@ -38,6 +38,7 @@ class _CLayout(ctypes.Structure):
         ("max_replicas", ctypes.c_int32),
         ("max_rank_natives", ctypes.c_int32),
         ("max_rank_spares", ctypes.c_int32),
+        ("ranks_per_domain", ctypes.c_int32),
         ("tables", ctypes.c_void_p),
     ]
 
@@ -137,6 +138,13 @@ class Layout:
 
     def ref(self):
         return ctypes.byref(self.c)
+
+    def with_domain(self, ranks_per_domain: int) -> "Layout":
+        """The same layout with replicas confined to domains of that many ranks (0: anywhere)."""
+        c = _CLayout.from_buffer_copy(self.c)
+        c.ranks_per_domain = int(ranks_per_domain)
+        return Layout(self.num_experts, self.num_ranks, self.num_phys, self.num_spare, self.max_replicas,
+                      self.tables, c)
 
 
 def ep_workspace_bytes(pairs_per_plan: int, num_plans: int, num_experts: int) -> int:

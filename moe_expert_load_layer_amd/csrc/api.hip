@@ -29,6 +29,7 @@ bool layout_ok(const ep_layout_t *L) {
     if (L->max_replicas != rho) return false;
     if (L->max_rank_natives < 0 || L->max_rank_natives > L->num_experts) return false;
     if (L->max_rank_spares < 0 || L->max_rank_spares > L->num_spare) return false;
+    if (L->ranks_per_domain < 0) return false;
     return aligned(L->tables, 4);
 }
 
@@ -118,6 +119,7 @@ int ep_layout_init(int32_t E, int32_t R, const int32_t *native_count, const int3
     out->max_replicas = R < 1 + (int32_t)S ? R : 1 + (int32_t)S;
     out->max_rank_natives = max_nat;
     out->max_rank_spares = max_sp;
+    out->ranks_per_domain = 0;
     out->tables = device_tables;
     return EP_OK;
 }

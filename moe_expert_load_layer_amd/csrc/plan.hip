@@ -26,6 +26,7 @@ namespace {
 
 struct PlanArgs {
     int32_t E, R, Phi, S, rho;
+    int32_t D;  // ranks per scale-up domain (0: no constraint)
     Tables T;
 };
 
@@ -106,8 +107,9 @@ __global__ __launch_bounds__(kWave) void plan_kernel_generic(const int32_t *__re
             if (lane < n) stamp[srank[islot[lane]]] = tries;
             __syncthreads();
             uint64_t best = 0;
+            const int hr = srank[hslot[e]];
             for (int r = lane; r < R; r += kWave) {
-                if (freec[r] > 0 && stamp[r] != tries) {
+                if (freec[r] > 0 && stamp[r] != tries && (a.D == 0 || r / a.D == hr / a.D)) {
                     const uint64_t k = ((uint64_t)inv((uint32_t)rl[r]) << 32) | inv((uint32_t)r);
                     best = k > best ? k : best;
                 }
@@ -398,7 +400,7 @@ __global__ __launch_bounds__(kWave) void plan_kernel_lanes(const int32_t *__rest
                 const int b = rl - q;
                 bool isnew = false;
                 if (replicate) {
-                    const bool elig = is_rank && freec > 0 && !inst;
+                    const bool elig = is_rank && freec > 0 && !inst && (a.D == 0 || lane / a.D == nr / a.D);
                     const int vmin = wave_min_i32(elig ? rl : 0x7fffffff);
                     const uint64_t em = __ballot(elig && rl == vmin);
                     if (em == 0) continue;
@@ -537,7 +539,8 @@ int plan_lanes_cfg(const ep_layout_t &L) {
 hipError_t launch_plan(const int32_t *load, int32_t P, const ep_layout_t &L, int32_t *phy2log,
                        int32_t *phy_quota, int32_t *logcnt, int32_t *log2phy, int32_t *steps,
                        uint32_t *status, hipStream_t s, int cfg) {
-    PlanArgs a{L.num_experts, L.num_ranks, L.num_phys, L.num_spare, L.max_replicas, tables_of(L)};
+    PlanArgs a{L.num_experts, L.num_ranks, L.num_phys, L.num_spare, L.max_replicas, L.ranks_per_domain,
+               tables_of(L)};
     const dim3 g((unsigned)P), b(kWave);
     const size_t lds = lanes_lds_bytes(L);
     switch (cfg) {

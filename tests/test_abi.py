@@ -50,18 +50,18 @@ def test_host_side_checks_without_gpu():
     assert 0 < a < b
     assert a % (129 * 4) == 0
     # null pointers are rejected before any device work
-    lay = ep._CLayout(12, 8, 16, 4, 5, 2, 1, None)
+    lay = ep._CLayout(12, 8, 16, 4, 5, 2, 1, 0, None)
     rc = L.ep_load_histogram(None, 512, 1, ctypes.byref(lay), None, None, 0, None, None)
     assert rc == ep.EP_ERR_INVALID_ARG
     rc = L.ep_plan_quota(None, 1, ctypes.byref(lay), None, None, None, None, None, None, None)
     assert rc == ep.EP_ERR_INVALID_ARG
     # inconsistent layout header (rho must be min(R, 1+S)) is rejected
-    lay_bad = ep._CLayout(12, 8, 16, 4, 4, 2, 1, ctypes.c_void_p(16))
+    lay_bad = ep._CLayout(12, 8, 16, 4, 4, 2, 1, 0, ctypes.c_void_p(16))
     rc = L.ep_balance_stats(ctypes.c_void_p(16), ctypes.c_void_p(16), 1, ctypes.byref(lay_bad),
                             ctypes.c_void_p(16), ctypes.c_void_p(16), None, None)
     assert rc == ep.EP_ERR_INVALID_ARG
     # slot fill needs a multiple of 16 bytes per expert
-    lay_ok = ep._CLayout(12, 8, 16, 4, 5, 2, 1, ctypes.c_void_p(16))
+    lay_ok = ep._CLayout(12, 8, 16, 4, 5, 2, 1, 0, ctypes.c_void_p(16))
     rc = L.ep_slot_fill(ctypes.c_void_p(16), 24, ctypes.c_void_p(16), ctypes.byref(lay_ok),
                         ctypes.c_void_p(16), None)
     assert rc == ep.EP_ERR_INVALID_ARG

@@ -393,3 +393,36 @@ def test_reroute_many_split_experts_in_one_subblock(dev):
     torch.cuda.synchronize()
     ref, _ = oracle.reroute(ids[0], E, pl.phy_quota, pl.log2phy, pl.logcnt)
     np.testing.assert_array_equal(_np(phys[0]), ref)
+
+
+# ------------------------------------------------ domain-constrained planner
+@pytest.mark.parametrize("name,D", [("qwen3_235b", 8), ("deepseek_v3", 8), ("glm_4_5", 8), ("stress", 8),
+                                    ("tiny", 2), ("qwen3_235b", 1), ("stress", 64)])
+def test_plan_domain_matches_oracle(dev, name, D):
+    wl, wls = _small(name, tokens=200, layers=3, mbs=2)
+    lay_o = oracle.Layout.from_workload(wl)
+    ids = W.make_ids(wls).numpy()
+    loads = np.stack([oracle.histogram(ids[p], wl.num_experts)[0] for p in range(ids.shape[0])])
+    refs = [oracle.plan(l, lay_o, D) for l in loads]
+    lay = ep.Layout.from_workload(wl, device=dev).with_domain(D)
+    out = ep.ep_plan_quota(torch.from_numpy(loads).to(dev), lay)
+    torch.cuda.synchronize()
+    _assert_plan_equal(out, refs)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_plan_domain_random_layouts(dev, seed):
+    # random layouts hit both planner kernels (rank-per-lane and generic)
+    rng = np.random.default_rng(500 + seed)
+    for it in range(8):
+        E, R, nc, ne, sc = W.random_layout(rng, max_experts=90, max_ranks=80, max_spare_per_rank=3)
+        lay_o = oracle.Layout.of(E, R, nc, ne, sc)
+        if lay_o.max_replicas > 64:
+            continue
+        D = int(rng.integers(1, R + 1))
+        loads = (rng.pareto(0.8, size=(2, E)) * 60).astype(np.int32)
+        refs = [oracle.plan(l, lay_o, D) for l in loads]
+        lay = ep.Layout.create(E, nc, ne, sc, device=dev).with_domain(D)
+        out = ep.ep_plan_quota(torch.from_numpy(loads).to(dev), lay)
+        torch.cuda.synchronize()
+        _assert_plan_equal(out, refs)
