@@ -224,6 +224,19 @@ def main(argv=None) -> int:
     next_rows.update({"grad_reduce_ms": red_ms, "grad_reduce_bytes": red_bytes,
                       "grad_reduce_GBps": red_bytes / (red_ms * 1e-3) / 1e9})
     del g_native, g_slot
+    # domain-constrained planner: replicas stay inside 8-rank scale-up domains
+    # (one xGMI node); the same loads, all plans in one launch
+    lay_d = lay.with_domain(8)
+    pl_d = ep.alloc_plan(P, lay_d, dev)
+    dom_ms = lat(lambda: ep.ep_plan_quota(load, lay_d, out=pl_d), 5) * 1e-3
+    st_d = torch.empty((P, 4), dtype=torch.int64, device=dev)
+    imb_d = torch.empty((P, 2), dtype=torch.float64, device=dev)
+    ep.ep_balance_stats(load, pl_d.phy_quota, lay_d, stats=st_d, imbalance=imb_d, want_rank_load=False)
+    imb_d_np = imb_d.cpu().numpy()
+    next_rows.update({"domain_plan_ranks_per_domain": 8,
+                      "domain_plan_us_per_layer_batched": dom_ms * 1e3 / P,
+                      "domain_imbalance_after_mean": float(imb_d_np[:, 1].mean()),
+                      "domain_imbalance_after_max": float(imb_d_np[:, 1].max())})
 
     traffic = None
     if TRAFFIC and TRAFFIC.get("kernel_sha") == _src_sha("slotfill.hip"):

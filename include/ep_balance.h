@@ -111,9 +111,12 @@ int ep_layout_init(int32_t num_experts, int32_t num_ranks, const int32_t *native
 
 /*
  * Workspace for one (ep_load_histogram, ep_reroute) pair, in bytes.  It carries
- * the per-sub-block expert counts (and after the histogram, their exclusive
- * prefix per expert) from the histogram to the reroute: pass the same buffer,
- * untouched in between, to both.  Grows as P * ceil(N / sub-block) * (E + 1) * 4.
+ * per-expert pair counts from the histogram to the reroute (and the dispatch
+ * layout): for every sub-block of consecutive pairs, how many pairs of each
+ * expert come before it in the plan, stored as a count within a segment of
+ * sub-blocks plus a per-segment base.  Pass the same buffer, untouched in
+ * between, with the same N and P.  Grows as P * (sub-blocks + segments + 1) *
+ * (E + 1) * 4, about 1/8 to 1/4 byte per pair.
  */
 size_t ep_workspace_bytes(int64_t pairs_per_plan, int32_t num_plans, int32_t num_experts);
 

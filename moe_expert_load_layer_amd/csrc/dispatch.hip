@@ -60,7 +60,7 @@ __device__ __forceinline__ int32_t position_of(const int2 *inst, int f, int n, i
 template <int W, bool STAGED>
 __global__ __launch_bounds__(W *kWave) void dispatch_kernel(
     const int32_t *__restrict__ ids, int64_t N, int32_t E, int32_t Phi, int32_t rho, int64_t sub,
-    int64_t nsb, const int32_t *__restrict__ ws, const int32_t *__restrict__ phy_quota,
+    int64_t nsb, int64_t sps, int64_t nseg, const int32_t *__restrict__ ws, const int32_t *__restrict__ phy_quota,
     const int32_t *__restrict__ log2phy, const int32_t *__restrict__ logcnt,
     int32_t *__restrict__ slot_offsets, int32_t *__restrict__ dpos, int32_t *__restrict__ dsrc) {
     extern __shared__ __align__(16) unsigned char sh_raw[];
@@ -129,16 +129,15 @@ __global__ __launch_bounds__(W *kWave) void dispatch_kernel(
     CellState *st = st_all + (size_t)wave * E;
     CellInfo *ci = ci_all + (size_t)wave * E;
     uint16_t *stage = stage_all + (size_t)wave * (STAGED ? sub : 0);
-    const int32_t *row0 = ws + ((int64_t)p * (nsb + 1) + sb) * E1;
-    const int32_t *row1 = row0 + E1;
+    const SubPrefix pre = sub_prefix(ws, p, sb, nsb, sps, nseg, E1);
     {
         int carry = 0;
         for (int c = 0; c < E; c += kWave) {
             const int e = c + lane;
             int32_t run = 0, cnt = 0, delta = kNoCell;
             if (e < E) {
-                run = row0[e];
-                cnt = row1[e] - run;
+                run = pre.start(e);
+                cnt = pre.end(e) - run;
                 const int f = rfirst[e], n = rcnt[e];
                 int lo = 0, hi = n;
                 while (lo < hi) {
@@ -244,10 +243,11 @@ size_t dispatch_lds_bytes(int E, int Phi, int waves, int64_t stage_pairs) {
            (size_t)(Phi + 1) * 4 + (size_t)E * 8 + (size_t)waves * stage_pairs * 2;
 }
 
-hipError_t launch_dispatch(const int32_t *ids, int64_t N, int32_t P, const ep_layout_t &L, int64_t sub,
-                           int64_t nsb, const int32_t *ws, const int32_t *phy_quota,
+hipError_t launch_dispatch(const int32_t *ids, int64_t N, int32_t P, const ep_layout_t &L,
+                           const SubGeom &g, const int32_t *ws, const int32_t *phy_quota,
                            const int32_t *log2phy, const int32_t *logcnt, int32_t *slot_offsets,
                            int32_t *dpos, int32_t *dsrc, hipStream_t s) {
+    const int64_t sub = g.sub, nsb = g.nsb, sps = g.sps, nseg = g.nseg;
     const int E = L.num_experts, Phi = L.num_phys, rho = L.max_replicas;
     // stage through LDS when a sub-block's pair indices fit (16-bit, 1 or 2 waves)
     int w = sub <= 65536 ? pick_dispatch_waves(E, Phi, sub) : 0;
@@ -260,7 +260,7 @@ hipError_t launch_dispatch(const int32_t *ids, int64_t N, int32_t P, const ep_la
     dim3 grid((unsigned)nblk, (unsigned)P);
 #define EP_DISPATCH(WV, ST)                                                                        \
     hipLaunchKernelGGL((dispatch_kernel<WV, ST>), grid, dim3(WV * kWave), lds, s, ids, N, E, Phi, rho, \
-                       sub, nsb, ws, phy_quota, log2phy, logcnt, slot_offsets, dpos, dsrc)
+                       sub, nsb, sps, nseg, ws, phy_quota, log2phy, logcnt, slot_offsets, dpos, dsrc)
     if (staged) {
         if (w == 4) EP_DISPATCH(4, true); else if (w == 2) EP_DISPATCH(2, true); else EP_DISPATCH(1, true);
     } else {

@@ -47,11 +47,23 @@ inline Tables tables_of(const ep_layout_t &L) {
 
 // ---------------------------------------------------------------------------
 // Sub-blocks: the pairs of one plan are cut into consecutive sub-blocks, one
-// per wave, in both the histogram and the reroute.  The histogram stores each
-// sub-block's expert counts (plus a count of invalid IDs in column E); the
-// scan turns them into exclusive per-expert offsets.  The size aims at ~8K
-// waves in a launch, keeps the count table under 1/4 byte per pair
-// (>= 16 (E+1) pairs), and is a power of two between 2048 and 32768.
+// per wave in the reroute and the dispatch layout.  The size aims at ~8K waves
+// in a launch, keeps the count table under 1/4 byte per pair (>= 16 (E+1)
+// pairs), and is a power of two between 2048 and 4096.
+//
+// Segments: the histogram gives each wave a segment of `sps` consecutive
+// sub-blocks (sps a power of two, so that launches of many plans have fewer,
+// longer waves).  The wave keeps a running per-expert count over its segment
+// and stores, for every sub-block but the segment's first, the count of the
+// segment's pairs before it (the in-segment prefix).  A small scan then turns
+// the segment totals into exclusive segment bases.  Workspace rows per plan
+// (each E + 1 ints, column E counting IDs >= E):
+//   rows [0, nsb)              in-segment prefix of sub-block sb (row of a
+//                              segment's first sub-block unused: it is 0)
+//   rows [nsb, nsb + nseg]     base[j] = pairs of segments < j; base[nseg]
+//                              is the plan's total per expert (its load)
+// so that the pairs of expert e before sub-block sb number
+//   in[sb][e] + base[sb / sps][e].
 // ---------------------------------------------------------------------------
 #ifndef EP_SUB_TARGET_WAVES
 #define EP_SUB_TARGET_WAVES 8192
@@ -61,6 +73,12 @@ inline Tables tables_of(const ep_layout_t &L) {
 #endif
 #ifndef EP_SUB_MIN
 #define EP_SUB_MIN 2048
+#endif
+#ifndef EP_HIST_TARGET_WAVES
+#define EP_HIST_TARGET_WAVES 8192
+#endif
+#ifndef EP_SEG_MAX
+#define EP_SEG_MAX 64
 #endif
 inline int64_t sub_pairs(int64_t N, int32_t P, int32_t E) {
     const int64_t tw = EP_SUB_TARGET_WAVES;
@@ -79,10 +97,58 @@ inline int64_t sub_pairs(int64_t N, int32_t P, int32_t E) {
 
 inline int64_t num_sub(int64_t N, int64_t sub) { return N <= 0 ? 0 : (N + sub - 1) / sub; }
 
-// per plan: one count row per sub-block plus one row of per-expert totals
+// sub-blocks per histogram segment
+inline int64_t seg_subs(int64_t nsb, int32_t P) {
+    const int64_t per = nsb * (int64_t)P / EP_HIST_TARGET_WAVES;
+    int64_t s = 1;
+    while (2 * s <= per && 2 * s <= EP_SEG_MAX) s <<= 1;
+#ifdef EP_SEG_FIXED
+    s = EP_SEG_FIXED;
+#endif
+    return s;
+}
+
+inline int64_t num_seg(int64_t nsb, int64_t sps) { return (nsb + sps - 1) / sps; }
+
+struct SubGeom {
+    int64_t sub, nsb, sps, nseg;
+};
+
+inline SubGeom sub_geom(int64_t N, int32_t P, int32_t E) {
+    SubGeom g;
+    g.sub = sub_pairs(N, P, E);
+    g.nsb = num_sub(N, g.sub);
+    g.sps = seg_subs(g.nsb, P);
+    g.nseg = num_seg(g.nsb, g.sps);
+    return g;
+}
+
 inline size_t ws_bytes(int64_t N, int32_t P, int32_t E) {
-    const int64_t sub = sub_pairs(N, P, E);
-    return (size_t)P * (size_t)(num_sub(N, sub) + 1) * (size_t)(E + 1) * sizeof(int32_t);
+    const SubGeom g = sub_geom(N, P, E);
+    return (size_t)P * (size_t)(g.nsb + g.nseg + 1) * (size_t)(E + 1) * sizeof(int32_t);
+}
+
+// Per-expert pair counts of plan p before sub-block sb (start) and before
+// sb + 1 (end), read from the workspace rows above.
+struct SubPrefix {
+    const int32_t *in0, *in1, *b0, *b1;
+    bool first, last;
+    __device__ __forceinline__ int32_t start(int e) const { return (first ? 0 : in0[e]) + b0[e]; }
+    __device__ __forceinline__ int32_t end(int e) const { return last ? b1[e] : in1[e] + b0[e]; }
+};
+
+__device__ __forceinline__ SubPrefix sub_prefix(const int32_t *ws, int p, int64_t sb, int64_t nsb,
+                                                int64_t sps, int64_t nseg, int E1) {
+    const int32_t *plan = ws + (int64_t)p * (nsb + nseg + 1) * E1;
+    const int64_t seg = sb / sps;
+    SubPrefix s;
+    s.in0 = plan + sb * E1;
+    s.in1 = s.in0 + E1;
+    s.b0 = plan + (nsb + seg) * E1;
+    s.b1 = s.b0 + E1;
+    s.first = sb == seg * sps;
+    s.last = sb + 1 == nsb || sb + 1 == (seg + 1) * sps;
+    return s;
 }
 
 // ---------------------------------------------------------------------------
@@ -185,9 +251,8 @@ __device__ __forceinline__ void wave_lds_fence() {
 // ---------------------------------------------------------------------------
 // launchers (defined in the .hip files; return hipError_t of the launch)
 // ---------------------------------------------------------------------------
-hipError_t launch_histogram(const int32_t *ids, int64_t N, int32_t P, int32_t E, int64_t sub,
-                            int64_t nsb, int32_t *ws, int32_t *load, uint32_t *status,
-                            hipStream_t s);
+hipError_t launch_histogram(const int32_t *ids, int64_t N, int32_t P, int32_t E, const SubGeom &g,
+                            int32_t *ws, int32_t *load, uint32_t *status, hipStream_t s);
 // cfg > 0 selects the rank-per-lane planner (32 * natives + spares registers
 // per lane, see plan_lanes_cfg); cfg == 0 selects the generic planner
 hipError_t launch_plan(const int32_t *load, int32_t P, const ep_layout_t &L, int32_t *phy2log,
@@ -196,12 +261,12 @@ hipError_t launch_plan(const int32_t *load, int32_t P, const ep_layout_t &L, int
 size_t plan_lds_bytes(const ep_layout_t &L);
 int plan_lanes_cfg(const ep_layout_t &L);
 hipError_t launch_reroute(const int32_t *ids, int64_t N, int32_t P, const ep_layout_t &L,
-                          int64_t sub, int64_t nsb, const int32_t *ws, const int32_t *phy_quota,
+                          const SubGeom &g, const int32_t *ws, const int32_t *phy_quota,
                           const int32_t *log2phy, const int32_t *logcnt, int32_t *out,
                           hipStream_t s);
 size_t reroute_lds_bytes(int E, int Phi, int waves);
-hipError_t launch_dispatch(const int32_t *ids, int64_t N, int32_t P, const ep_layout_t &L, int64_t sub,
-                           int64_t nsb, const int32_t *ws, const int32_t *phy_quota,
+hipError_t launch_dispatch(const int32_t *ids, int64_t N, int32_t P, const ep_layout_t &L,
+                           const SubGeom &g, const int32_t *ws, const int32_t *phy_quota,
                            const int32_t *log2phy, const int32_t *logcnt, int32_t *slot_offsets,
                            int32_t *dpos, int32_t *dsrc, hipStream_t s);
 size_t dispatch_lds_bytes(int E, int Phi, int waves, int64_t stage_pairs);

@@ -2,13 +2,15 @@
 // the key designs: the global load is read after the gate, before planning).
 //
 // Two kernels:
-//   hist_kernel  one wave per sub-block of consecutive pairs; counts into a
+//   hist_kernel  one wave per segment of consecutive sub-blocks; counts into a
 //                wave-private LDS histogram (E bins + one bin for IDs >= E)
-//                with LDS integer atomics, then writes the row to the
-//                workspace.  The IDs stream in as 16-byte loads.
-//   scan_kernel  per (plan, 64 experts): turns the sub-block rows into
-//                exclusive per-expert offsets in place (what the reroute needs
-//                for a stable order) and writes load[p][e] = total and the
+//                with LDS integer atomics.  Before each sub-block but the
+//                segment's first it stores the running counts (the sub-block's
+//                in-segment prefix); at the segment's end it stores the
+//                segment's totals.  The IDs stream in as 16-byte loads.
+//   scan_kernel  per (plan, 64 experts): inclusive scan of the segment totals
+//                in place, which leaves base[j] = pairs of segments < j and
+//                base[nseg] = the plan's total; writes load[p][e] and the
 //                plan's status word.
 // Integer counts only, so the result does not depend on atomic order.
 #include "ep_internal.h"
@@ -25,24 +27,25 @@ namespace {
 constexpr int kHistWaves = EP_HIST_WAVES;
 
 __global__ __launch_bounds__(kHistWaves * kWave) void hist_kernel(
-    const int32_t *__restrict__ ids, int64_t N, int32_t E, int64_t sub, int64_t nsb,
-    int32_t *__restrict__ ws) {
+    const int32_t *__restrict__ ids, int64_t N, int32_t E, int64_t sub, int64_t nsb, int64_t sps,
+    int64_t nseg, int32_t *__restrict__ ws) {
     extern __shared__ int32_t sh_hist[];
     const int wave = threadIdx.x / kWave;
     const int lane = threadIdx.x % kWave;
     const int E1 = E + 1;
     int32_t *h = sh_hist + wave * E1;
-    const int64_t sb = (int64_t)blockIdx.x * kHistWaves + wave;
+    const int64_t seg = (int64_t)blockIdx.x * kHistWaves + wave;
     const int p = blockIdx.y;
-    if (sb >= nsb) return;  // wave-private LDS: no block barrier below
+    if (seg >= nseg) return;  // wave-private LDS: no block barrier below
 
     for (int e = lane; e < E1; e += kWave) h[e] = 0;
     wave_lds_fence();
 
-    const int64_t begin = sb * sub;
-    const int64_t end = (begin + sub < N) ? begin + sub : N;
+    int32_t *plan_ws = ws + (int64_t)p * (nsb + nseg + 1) * E1;
     const int32_t *src = ids + (int64_t)p * N;
     const uint32_t uE = (uint32_t)E;
+    const int64_t sb0 = seg * sps;
+    const int64_t sb1 = (sb0 + sps < nsb) ? sb0 + sps : nsb;
     int nbad = 0;
 
     auto count = [&](int32_t v) {
@@ -53,44 +56,54 @@ __global__ __launch_bounds__(kHistWaves * kWave) void hist_kernel(
         }
     };
 
-    int64_t i = begin;
-    // 16-byte path: the plan row and sub-block start are 16-byte aligned
-    if (((uintptr_t)(src + begin) & 15) == 0) {
-        const int64_t nvec = (end - begin) / 4;
-        const i32x4 *v4 = reinterpret_cast<const i32x4 *>(src + begin);
-        constexpr int U = EP_HIST_UNROLL;
-        int64_t k = lane;
-        for (; k + (U - 1) * kWave < nvec; k += U * kWave) {
-            i32x4 x[U];
+    for (int64_t sb = sb0; sb < sb1; sb++) {
+        if (sb != sb0) {
+            // in-segment prefix of this sub-block (IDs >= E included)
+            if (nbad) atomicAdd(&h[E], nbad);
+            nbad = 0;
+            wave_lds_fence();
+            int32_t *row = plan_ws + sb * E1;
+            for (int e = lane; e < E1; e += kWave) row[e] = h[e];
+        }
+        const int64_t begin = sb * sub;
+        const int64_t end = (begin + sub < N) ? begin + sub : N;
+        int64_t i = begin;
+        // 16-byte path: the plan row and sub-block start are 16-byte aligned
+        if (((uintptr_t)(src + begin) & 15) == 0) {
+            const int64_t nvec = (end - begin) / 4;
+            const i32x4 *v4 = reinterpret_cast<const i32x4 *>(src + begin);
+            constexpr int U = EP_HIST_UNROLL;
+            int64_t k = lane;
+            for (; k + (U - 1) * kWave < nvec; k += U * kWave) {
+                i32x4 x[U];
 #pragma unroll
-            for (int u = 0; u < U; u++) x[u] = __builtin_nontemporal_load(v4 + k + u * kWave);
+                for (int u = 0; u < U; u++) x[u] = __builtin_nontemporal_load(v4 + k + u * kWave);
 #pragma unroll
-            for (int u = 0; u < U; u++) {
-                count(x[u].x); count(x[u].y); count(x[u].z); count(x[u].w);
+                for (int u = 0; u < U; u++) {
+                    count(x[u].x); count(x[u].y); count(x[u].z); count(x[u].w);
+                }
             }
+            for (; k < nvec; k += kWave) {
+                const i32x4 x = __builtin_nontemporal_load(v4 + k);
+                count(x.x); count(x.y); count(x.z); count(x.w);
+            }
+            i = begin + nvec * 4;
         }
-        for (; k < nvec; k += kWave) {
-            const i32x4 x = __builtin_nontemporal_load(v4 + k);
-            count(x.x); count(x.y); count(x.z); count(x.w);
-        }
-        i = begin + nvec * 4;
+        for (int64_t j = i + lane; j < end; j += kWave) count(src[j]);
     }
-    for (int64_t j = i + lane; j < end; j += kWave) count(src[j]);
     if (nbad) atomicAdd(&h[E], nbad);
     wave_lds_fence();
-
-    int32_t *row = ws + ((int64_t)p * (nsb + 1) + sb) * E1;
+    // segment totals go one row below the segment's base row; the scan makes
+    // the rows inclusive in place
+    int32_t *row = plan_ws + (nsb + seg + 1) * E1;
     for (int e = lane; e < E1; e += kWave) row[e] = h[e];
 }
 
 constexpr int kScanWaves = 16;
 constexpr int kScanUnroll = 8;
 
-// Workspace rows per plan: nsb sub-block rows, then one row of per-expert
-// totals (the plan's load), which lets the reroute skip ranking pairs of an
-// expert whose single instance takes all of its pairs.
 __global__ __launch_bounds__(kScanWaves * kWave) void scan_kernel(
-    int32_t *__restrict__ ws, int64_t nsb, int32_t E, int32_t *__restrict__ load,
+    int32_t *__restrict__ ws, int64_t nsb, int64_t nseg, int32_t E, int32_t *__restrict__ load,
     uint32_t *__restrict__ status) {
     __shared__ int32_t part[kScanWaves][kWave];
     const int wave = threadIdx.x / kWave;
@@ -98,10 +111,11 @@ __global__ __launch_bounds__(kScanWaves * kWave) void scan_kernel(
     const int E1 = E + 1;
     const int p = blockIdx.y;
     const int col = blockIdx.x * kWave + lane;
-    int32_t *base = ws + (int64_t)p * (nsb + 1) * E1;
-    const int64_t seg = (nsb + kScanWaves - 1) / kScanWaves;
-    const int64_t b0 = wave * seg < nsb ? wave * seg : nsb;
-    const int64_t b1 = (b0 + seg < nsb) ? b0 + seg : nsb;
+    // base rows of the plan; rows 1..nseg hold segment totals on entry
+    int32_t *base = ws + ((int64_t)p * (nsb + nseg + 1) + nsb) * E1;
+    const int64_t per = (nseg + kScanWaves - 1) / kScanWaves;
+    const int64_t b0 = 1 + (wave * per < nseg ? wave * per : nseg);
+    const int64_t b1 = (b0 + per < nseg + 1) ? b0 + per : nseg + 1;
     const bool on = col < E1;
 
     int32_t sum = 0;
@@ -118,12 +132,10 @@ __global__ __launch_bounds__(kScanWaves * kWave) void scan_kernel(
     }
     part[wave][lane] = sum;
     __syncthreads();
-    int32_t run = 0, total = 0;
-    for (int w = 0; w < kScanWaves; w++) {
-        if (w < wave) run += part[w][lane];
-        total += part[w][lane];
-    }
+    int32_t run = 0;
+    for (int w = 0; w < wave; w++) run += part[w][lane];
     if (on) {
+        if (wave == 0) base[col] = 0;
         int64_t b = b0;
         for (; b + kScanUnroll <= b1; b += kScanUnroll) {
             int32_t c[kScanUnroll];
@@ -131,38 +143,37 @@ __global__ __launch_bounds__(kScanWaves * kWave) void scan_kernel(
             for (int u = 0; u < kScanUnroll; u++) c[u] = base[(b + u) * E1 + col];
 #pragma unroll
             for (int u = 0; u < kScanUnroll; u++) {
-                base[(b + u) * E1 + col] = run;
                 run += c[u];
+                base[(b + u) * E1 + col] = run;
             }
         }
         for (; b < b1; b++) {
-            const int32_t c = base[b * E1 + col];
+            run += base[b * E1 + col];
             base[b * E1 + col] = run;
-            run += c;
         }
-        if (wave == 0) {
-            base[nsb * E1 + col] = total;
-            if (col < E) load[(int64_t)p * E + col] = total;
-            else status[p] = total > 0 ? (uint32_t)EP_STATUS_BAD_ID : 0u;
+        if (wave == kScanWaves - 1) {
+            // the last wave's running sum is the plan's total
+            if (col < E) load[(int64_t)p * E + col] = run;
+            else status[p] = run > 0 ? (uint32_t)EP_STATUS_BAD_ID : 0u;
         }
     }
 }
 
 }  // namespace
 
-hipError_t launch_histogram(const int32_t *ids, int64_t N, int32_t P, int32_t E, int64_t sub,
-                            int64_t nsb, int32_t *ws, int32_t *load, uint32_t *status,
-                            hipStream_t s) {
-    if (nsb > 0) {
-        dim3 grid((unsigned)((nsb + kHistWaves - 1) / kHistWaves), (unsigned)P);
+hipError_t launch_histogram(const int32_t *ids, int64_t N, int32_t P, int32_t E, const SubGeom &g,
+                            int32_t *ws, int32_t *load, uint32_t *status, hipStream_t s) {
+    if (g.nseg > 0) {
+        dim3 grid((unsigned)((g.nseg + kHistWaves - 1) / kHistWaves), (unsigned)P);
         const size_t lds = (size_t)kHistWaves * (E + 1) * sizeof(int32_t);
-        hipLaunchKernelGGL(hist_kernel, grid, dim3(kHistWaves * kWave), lds, s, ids, N, E, sub,
-                           nsb, ws);
+        hipLaunchKernelGGL(hist_kernel, grid, dim3(kHistWaves * kWave), lds, s, ids, N, E, g.sub,
+                           g.nsb, g.sps, g.nseg, ws);
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
     dim3 g2((unsigned)((E + 1 + kWave - 1) / kWave), (unsigned)P);
-    hipLaunchKernelGGL(scan_kernel, g2, dim3(kScanWaves * kWave), 0, s, ws, nsb, E, load, status);
+    hipLaunchKernelGGL(scan_kernel, g2, dim3(kScanWaves * kWave), 0, s, ws, g.nsb, g.nseg, E, load,
+                       status);
     return hipGetLastError();
 }
 

@@ -144,7 +144,7 @@ __device__ __forceinline__ void resolve_split(const int32_t (&x)[K], int32_t (&c
 template <int W>
 __global__ __launch_bounds__(W *kWave) void reroute_kernel(
     const int32_t *__restrict__ ids, int64_t N, int32_t E, int32_t Phi, int32_t rho, int64_t sub,
-    int64_t nsb, const int32_t *__restrict__ ws, const int32_t *__restrict__ phy_quota,
+    int64_t nsb, int64_t sps, int64_t nseg, const int32_t *__restrict__ ws, const int32_t *__restrict__ phy_quota,
     const int32_t *__restrict__ log2phy, const int32_t *__restrict__ logcnt,
     int32_t *__restrict__ out) {
     extern __shared__ __align__(16) unsigned char sh_raw[];
@@ -201,15 +201,14 @@ __global__ __launch_bounds__(W *kWave) void reroute_kernel(
     int32_t *srun = srun_all + (size_t)wave * E;
     int32_t *sidx = sidx_all + (size_t)wave * kWave;
     // --- per-expert code for this sub-block
-    const int32_t *row0 = ws + ((int64_t)p * (nsb + 1) + sb) * E1;
-    const int32_t *row1 = row0 + E1;  // next prefix row; after the last sub-block, the totals
+    const SubPrefix pre = sub_prefix(ws, p, sb, nsb, sps, nseg, E1);
     int nsplit = 0;
     for (int e0 = 0; e0 < E; e0 += kWave) {
         const int e = e0 + lane;
         int32_t cd = -1, run = 0;
         if (e < E) {
-            run = row0[e];
-            const int32_t nxt = row1[e];
+            run = pre.start(e);
+            const int32_t nxt = pre.end(e);
             const int f = rfirst[e], n = rcnt[e];
             const int t = first_above(inst + f, n, run);
             if (nxt > run && t < n) cd = nxt <= inst[f + t].x ? inst[f + t].y : kSplit;
@@ -312,9 +311,10 @@ size_t reroute_lds_bytes(int E, int Phi, int waves) {
 }
 
 hipError_t launch_reroute(const int32_t *ids, int64_t N, int32_t P, const ep_layout_t &L,
-                          int64_t sub, int64_t nsb, const int32_t *ws, const int32_t *phy_quota,
+                          const SubGeom &g, const int32_t *ws, const int32_t *phy_quota,
                           const int32_t *log2phy, const int32_t *logcnt, int32_t *out,
                           hipStream_t s) {
+    const int64_t sub = g.sub, nsb = g.nsb, sps = g.sps, nseg = g.nseg;
     if (nsb == 0) return hipSuccess;
     const int E = L.num_experts, Phi = L.num_phys, rho = L.max_replicas;
     const int w = pick_waves(E, Phi);
@@ -324,19 +324,19 @@ hipError_t launch_reroute(const int32_t *ids, int64_t N, int32_t P, const ep_lay
     switch (w) {
         case 8:
             hipLaunchKernelGGL(reroute_kernel<8>, grid, dim3(8 * kWave), lds, s, ids, N, E, Phi,
-                               rho, sub, nsb, ws, phy_quota, log2phy, logcnt, out);
+                               rho, sub, nsb, sps, nseg, ws, phy_quota, log2phy, logcnt, out);
             break;
         case 4:
             hipLaunchKernelGGL(reroute_kernel<4>, grid, dim3(4 * kWave), lds, s, ids, N, E, Phi,
-                               rho, sub, nsb, ws, phy_quota, log2phy, logcnt, out);
+                               rho, sub, nsb, sps, nseg, ws, phy_quota, log2phy, logcnt, out);
             break;
         case 2:
             hipLaunchKernelGGL(reroute_kernel<2>, grid, dim3(2 * kWave), lds, s, ids, N, E, Phi,
-                               rho, sub, nsb, ws, phy_quota, log2phy, logcnt, out);
+                               rho, sub, nsb, sps, nseg, ws, phy_quota, log2phy, logcnt, out);
             break;
         default:
             hipLaunchKernelGGL(reroute_kernel<1>, grid, dim3(kWave), lds, s, ids, N, E, Phi, rho,
-                               sub, nsb, ws, phy_quota, log2phy, logcnt, out);
+                               sub, nsb, sps, nseg, ws, phy_quota, log2phy, logcnt, out);
             break;
     }
     return hipGetLastError();

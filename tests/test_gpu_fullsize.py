@@ -95,3 +95,24 @@ def test_fullsize_slot_fill(dev, name):
                     assert np.all(got == 0x7FC1), f"plan {p} empty slot {o} was written"
     del weights, slot
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name", ["qwen3_235b", "deepseek_v3"])
+def test_fullsize_domain_plan(dev, name):
+    # all plans in one launch with replicas confined to 8-rank domains
+    wl = W.get(name)
+    print(f"[fullsize-domain] {name}: P={wl.num_plans} R={wl.num_ranks} D=8", flush=True)
+    ids = W.make_ids(wl, device=dev)
+    lay = ep.Layout.from_workload(wl, device=dev).with_domain(8)
+    load, _, _ = ep.ep_load_histogram(ids, lay)
+    out = ep.ep_plan_quota(load, lay)
+    torch.cuda.synchronize()
+    del ids
+    load_h = load.cpu().numpy()
+    got = {k: getattr(out, k).cpu().numpy() for k in ("phy2log", "phy_quota", "logcnt", "log2phy", "steps")}
+    lay_o = oracle.Layout.from_workload(wl)
+    for p in range(wl.num_plans):
+        pl = oracle.plan(load_h[p], lay_o, 8)
+        for k in ("phy2log", "phy_quota", "logcnt", "log2phy"):
+            assert np.array_equal(got[k][p], getattr(pl, k)), f"{k} plan {p}"
+        assert got["steps"][p] == pl.steps
