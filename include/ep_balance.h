@@ -129,7 +129,8 @@ size_t ep_workspace_bytes(int64_t pairs_per_plan, int32_t num_plans, int32_t num
  *   load      device int32 [P][E] (written)
  *   ws        device, >= ep_workspace_bytes(N, P, E) bytes, 16-byte aligned
  *   status    device uint32 [P] (written: EP_STATUS_BAD_ID or 0)
- * N may be 0 (loads become 0).  Requires N < 2^31, 1 <= P <= 65535.
+ * N may be 0 (loads become 0).  Requires N < 2^31, 1 <= P <= 65535 and
+ * E <= 2047 (eight LDS histograms of E + 1 counters in a workgroup).
  */
 int ep_load_histogram(const int32_t *topk_ids, int64_t pairs_per_plan, int32_t num_plans,
                       const ep_layout_t *layout, int32_t *load, void *ws, size_t ws_bytes,

@@ -134,7 +134,7 @@ int ep_load_histogram(const int32_t *topk_ids, int64_t N, int32_t P, const ep_la
                       ep_stream_t stream) {
     if (!layout_ok(layout) || !pairs_ok(topk_ids, N, P) || !load || !status) return EP_ERR_INVALID_ARG;
     const int E = layout->num_experts;
-    if ((size_t)4 * (E + 1) * 4 > kMaxLds) return EP_ERR_INVALID_ARG;
+    if ((size_t)kSegSubs * (E + 1) * 4 > kMaxLds) return EP_ERR_INVALID_ARG;
     const size_t need = ws_bytes(N, P, E);
     if (ws_size < need || (need > 0 && (!ws || !aligned(ws, 16)))) return EP_ERR_INVALID_ARG;
     return hip_rc(launch_histogram(topk_ids, N, P, E, sub_geom(N, P, E), static_cast<int32_t *>(ws), load, status, as_stream(stream)));

@@ -51,13 +51,13 @@ inline Tables tables_of(const ep_layout_t &L) {
 // in a launch, keeps the count table under 1/4 byte per pair (>= 16 (E+1)
 // pairs), and is a power of two between 2048 and 4096.
 //
-// Segments: the histogram gives each wave a segment of `sps` consecutive
-// sub-blocks (sps a power of two, so that launches of many plans have fewer,
-// longer waves).  The wave keeps a running per-expert count over its segment
-// and stores, for every sub-block but the segment's first, the count of the
-// segment's pairs before it (the in-segment prefix).  A small scan then turns
-// the segment totals into exclusive segment bases.  Workspace rows per plan
-// (each E + 1 ints, column E counting IDs >= E):
+// Segments: the histogram gives each workgroup a segment of `sps`
+// consecutive sub-blocks, one per wave.  After counting, each wave stores the
+// count of the segment's pairs before its sub-block (the in-segment prefix,
+// summed over the lower waves' LDS histograms) and the last wave the
+// segment's totals.  A small scan then turns the segment totals into
+// exclusive segment bases.  Workspace rows per plan (each E + 1 ints, column
+// E counting IDs >= E):
 //   rows [0, nsb)              in-segment prefix of sub-block sb (row of a
 //                              segment's first sub-block unused: it is 0)
 //   rows [nsb, nsb + nseg]     base[j] = pairs of segments < j; base[nseg]
@@ -74,12 +74,10 @@ inline Tables tables_of(const ep_layout_t &L) {
 #ifndef EP_SUB_MIN
 #define EP_SUB_MIN 2048
 #endif
-#ifndef EP_HIST_TARGET_WAVES
-#define EP_HIST_TARGET_WAVES 8192
+#ifndef EP_SEG_SUBS
+#define EP_SEG_SUBS 8
 #endif
-#ifndef EP_SEG_MAX
-#define EP_SEG_MAX 64
-#endif
+constexpr int kSegSubs = EP_SEG_SUBS;  // sub-blocks per segment = waves per histogram workgroup
 inline int64_t sub_pairs(int64_t N, int32_t P, int32_t E) {
     const int64_t tw = EP_SUB_TARGET_WAVES;
     int64_t want = (N * (int64_t)P + tw - 1) / tw;
@@ -98,15 +96,7 @@ inline int64_t sub_pairs(int64_t N, int32_t P, int32_t E) {
 inline int64_t num_sub(int64_t N, int64_t sub) { return N <= 0 ? 0 : (N + sub - 1) / sub; }
 
 // sub-blocks per histogram segment
-inline int64_t seg_subs(int64_t nsb, int32_t P) {
-    const int64_t per = nsb * (int64_t)P / EP_HIST_TARGET_WAVES;
-    int64_t s = 1;
-    while (2 * s <= per && 2 * s <= EP_SEG_MAX) s <<= 1;
-#ifdef EP_SEG_FIXED
-    s = EP_SEG_FIXED;
-#endif
-    return s;
-}
+inline int64_t seg_subs(int64_t, int32_t) { return kSegSubs; }
 
 inline int64_t num_seg(int64_t nsb, int64_t sps) { return (nsb + sps - 1) / sps; }
 

@@ -2,12 +2,13 @@
 // the key designs: the global load is read after the gate, before planning).
 //
 // Two kernels:
-//   hist_kernel  one wave per segment of consecutive sub-blocks; counts into a
-//                wave-private LDS histogram (E bins + one bin for IDs >= E)
-//                with LDS integer atomics.  Before each sub-block but the
-//                segment's first it stores the running counts (the sub-block's
-//                in-segment prefix); at the segment's end it stores the
-//                segment's totals.  The IDs stream in as 16-byte loads.
+//   hist_kernel  one workgroup per segment of kSegSubs consecutive
+//                sub-blocks, one wave per sub-block; each wave counts into
+//                its own LDS histogram (E bins + one bin for IDs >= E) with
+//                LDS integer atomics, the IDs streaming in as 16-byte loads.
+//                After a barrier each wave stores its sub-block's in-segment
+//                prefix (the sum of the lower waves' histograms) and the last
+//                wave also the segment's totals.
 //   scan_kernel  per (plan, 64 experts): inclusive scan of the segment totals
 //                in place, which leaves base[j] = pairs of segments < j and
 //                base[nseg] = the plan's total; writes load[p][e] and the
@@ -18,36 +19,29 @@
 namespace ep {
 namespace {
 
-#ifndef EP_HIST_WAVES
-#define EP_HIST_WAVES 4
-#endif
 #ifndef EP_HIST_UNROLL
 #define EP_HIST_UNROLL 4
 #endif
-constexpr int kHistWaves = EP_HIST_WAVES;
+constexpr int kHistWaves = kSegSubs;
 
 __global__ __launch_bounds__(kHistWaves * kWave) void hist_kernel(
-    const int32_t *__restrict__ ids, int64_t N, int32_t E, int64_t sub, int64_t nsb, int64_t sps,
+    const int32_t *__restrict__ ids, int64_t N, int32_t E, int64_t sub, int64_t nsb,
     int64_t nseg, int32_t *__restrict__ ws) {
     extern __shared__ int32_t sh_hist[];
     const int wave = threadIdx.x / kWave;
     const int lane = threadIdx.x % kWave;
     const int E1 = E + 1;
     int32_t *h = sh_hist + wave * E1;
-    const int64_t seg = (int64_t)blockIdx.x * kHistWaves + wave;
+    const int64_t seg = blockIdx.x;
     const int p = blockIdx.y;
-    if (seg >= nseg) return;  // wave-private LDS: no block barrier below
+    const int64_t sb = seg * kHistWaves + wave;
 
     for (int e = lane; e < E1; e += kWave) h[e] = 0;
     wave_lds_fence();
 
-    int32_t *plan_ws = ws + (int64_t)p * (nsb + nseg + 1) * E1;
     const int32_t *src = ids + (int64_t)p * N;
     const uint32_t uE = (uint32_t)E;
-    const int64_t sb0 = seg * sps;
-    const int64_t sb1 = (sb0 + sps < nsb) ? sb0 + sps : nsb;
     int nbad = 0;
-
     auto count = [&](int32_t v) {
         if ((uint32_t)v < uE) {
             atomicAdd(&h[v], 1);
@@ -56,15 +50,7 @@ __global__ __launch_bounds__(kHistWaves * kWave) void hist_kernel(
         }
     };
 
-    for (int64_t sb = sb0; sb < sb1; sb++) {
-        if (sb != sb0) {
-            // in-segment prefix of this sub-block (IDs >= E included)
-            if (nbad) atomicAdd(&h[E], nbad);
-            nbad = 0;
-            wave_lds_fence();
-            int32_t *row = plan_ws + sb * E1;
-            for (int e = lane; e < E1; e += kWave) row[e] = h[e];
-        }
+    if (sb < nsb) {  // waves past the plan's last sub-block keep an empty histogram
         const int64_t begin = sb * sub;
         const int64_t end = (begin + sub < N) ? begin + sub : N;
         int64_t i = begin;
@@ -90,13 +76,28 @@ __global__ __launch_bounds__(kHistWaves * kWave) void hist_kernel(
             i = begin + nvec * 4;
         }
         for (int64_t j = i + lane; j < end; j += kWave) count(src[j]);
+        if (nbad) atomicAdd(&h[E], nbad);
     }
-    if (nbad) atomicAdd(&h[E], nbad);
-    wave_lds_fence();
-    // segment totals go one row below the segment's base row; the scan makes
-    // the rows inclusive in place
-    int32_t *row = plan_ws + (nsb + seg + 1) * E1;
-    for (int e = lane; e < E1; e += kWave) row[e] = h[e];
+    __syncthreads();
+
+    int32_t *plan_ws = ws + (int64_t)p * (nsb + nseg + 1) * E1;
+    const bool last = wave == kHistWaves - 1;
+    if (wave > 0 && (sb < nsb || last)) {
+        int32_t *row = plan_ws + sb * E1;
+        // segment totals go one row below the segment's base row; the scan
+        // makes the rows inclusive in place
+        int32_t *tot = plan_ws + (nsb + seg + 1) * E1;
+        for (int e = lane; e < E1; e += kWave) {
+            int32_t pre = 0;
+            for (int w = 0; w < wave; w++) pre += sh_hist[w * E1 + e];
+            if (sb < nsb) row[e] = pre;
+            if (last) tot[e] = pre + h[e];
+        }
+    }
+    if (kHistWaves == 1) {
+        int32_t *tot = plan_ws + (nsb + seg + 1) * E1;
+        for (int e = lane; e < E1; e += kWave) tot[e] = h[e];
+    }
 }
 
 constexpr int kScanWaves = 16;
@@ -163,11 +164,12 @@ __global__ __launch_bounds__(kScanWaves * kWave) void scan_kernel(
 
 hipError_t launch_histogram(const int32_t *ids, int64_t N, int32_t P, int32_t E, const SubGeom &g,
                             int32_t *ws, int32_t *load, uint32_t *status, hipStream_t s) {
+    if (g.sps != kHistWaves) return hipErrorInvalidValue;
     if (g.nseg > 0) {
-        dim3 grid((unsigned)((g.nseg + kHistWaves - 1) / kHistWaves), (unsigned)P);
+        dim3 grid((unsigned)g.nseg, (unsigned)P);
         const size_t lds = (size_t)kHistWaves * (E + 1) * sizeof(int32_t);
         hipLaunchKernelGGL(hist_kernel, grid, dim3(kHistWaves * kWave), lds, s, ids, N, E, g.sub,
-                           g.nsb, g.sps, g.nseg, ws);
+                           g.nsb, g.nseg, ws);
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
