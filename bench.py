@@ -137,14 +137,14 @@ def main(argv=None) -> int:
         e.record(stream)
         return e
 
-    rec = dict(hist=[], plan=[], reroute=[], path=[], stats=[], fill=[])
+    rec = dict(path=[], stats=[], fill=[])
 
     def step(record: bool):
+        # events only at the ends of the path: an event between two kernels
+        # leaves the GPU idle for a few microseconds
         a = ev()
         ep.ep_load_histogram(ids, lay, load=load, ws=ws, status=status)
-        b = ev()
         ep.ep_plan_quota(load, lay, out=plan, status=status)
-        c = ev()
         ep.ep_reroute(ids, lay, plan.phy_quota, plan.log2phy, plan.logcnt, ws, phys_ids=phys)
         d = ev()
         ep.ep_balance_stats(load, plan.phy_quota, lay, stats=stats, imbalance=imb, want_rank_load=False)
@@ -155,7 +155,6 @@ def main(argv=None) -> int:
             ep.ep_slot_fill(weights, plan.phy2log[l], lay, slot)
             fills.append((x, ev()))
         if record:
-            rec["hist"].append((a, b)); rec["plan"].append((b, c)); rec["reroute"].append((c, d))
             rec["path"].append((a, d)); rec["stats"].append((d, f)); rec["fill"].extend(fills)
 
     for _ in range(args.warmup):
@@ -177,8 +176,6 @@ def main(argv=None) -> int:
     fill_bytes = 2.0 * bpe * used                       # per layer (launch)
     fill_ms = np.array(ms["fill"]).reshape(args.steps, P).mean(axis=0)
     fill_gbps = float(fill_bytes.mean() / (fill_ms.mean() * 1e-3) / 1e9)
-    hist_gbps = 4.0 * P * N / (statistics.mean(ms["hist"]) * 1e-3) / 1e9
-    rr_gbps = 8.0 * P * N / (statistics.mean(ms["reroute"]) * 1e-3) / 1e9
     imb_np = imb.cpu().numpy()
 
     # single-plan latencies (one layer, as a real forward pass sees them)
@@ -191,6 +188,14 @@ def main(argv=None) -> int:
             xs.append((a, b))
         torch.cuda.synchronize()
         return statistics.median(_elapsed(xs)) * 1e3   # us
+
+    # the path's phases one at a time, all plans per launch
+    ph_hist = lat(lambda: ep.ep_load_histogram(ids, lay, load=load, ws=ws, status=status), 10) * 1e-3
+    ph_plan = lat(lambda: ep.ep_plan_quota(load, lay, out=plan, status=status), 10) * 1e-3
+    ph_rr = lat(lambda: ep.ep_reroute(ids, lay, plan.phy_quota, plan.log2phy, plan.logcnt, ws,
+                                      phys_ids=phys), 10) * 1e-3
+    hist_gbps = 4.0 * P * N / (ph_hist * 1e-3) / 1e9
+    rr_gbps = 8.0 * P * N / (ph_rr * 1e-3) / 1e9
 
     ids1 = ids[:1]
     load1 = load[:1].clone()
@@ -264,12 +269,13 @@ def main(argv=None) -> int:
                      "traffic": traffic,
                      "bytes_per_launch": float(fill_bytes.mean()),
                      "launch_ms": float(fill_ms.mean())},
-        "phases_ms_per_step": {k: statistics.mean(v) if k != "fill" else float(fill_ms.sum())
-                               for k, v in ms.items()},
+        "phases_ms_per_step": {"path": path_ms, "stats": statistics.mean(ms["stats"]),
+                               "fill": float(fill_ms.sum())},
+        "phases_ms_alone": {"hist": ph_hist, "plan": ph_plan, "reroute": ph_rr},
         "kernels": {
             "hist_GBps": hist_gbps, "hist_frac": hist_gbps / HBM_PEAK_GBPS,
             "reroute_GBps": rr_gbps, "reroute_frac": rr_gbps / HBM_PEAK_GBPS,
-            "plan_us_per_layer_batched": statistics.mean(ms["plan"]) * 1e3 / P,
+            "plan_us_per_layer_batched": ph_plan * 1e3 / P,
             "plan_us_single_layer": lat_plan,
             "hist_us_single_layer": lat_hist,
             "reroute_us_single_layer": lat_rr,
