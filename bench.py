@@ -6,6 +6,9 @@ per rank, 94 MoE layers):
   ep_load_histogram (94 plans) -> ep_plan_quota (94) -> ep_reroute (94)
   -> ep_balance_stats (94) -> ep_slot_fill once per layer (94 launches into the
   one cross-layer slot buffer, 3x4096x1536 bf16 per expert).
+The first three run as --chunks chunks of plans overlapped across three streams
+(the planner of one chunk under the histogram or reroute of another); the same
+path as three launches on one stream is timed beside it.
 Inputs are synthetic, seeded, and resident in HBM before timing starts.
 
 value = (token,k) pairs per second through hist + plan + reroute (HIP events
@@ -85,6 +88,10 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", default="qwen3_235b")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work (0 = skip)")
     ap.add_argument("--latency-reps", type=int, default=30)
+    ap.add_argument("--chunks", default="auto",
+                    help="plans per step cut into chunks overlapped across streams: 'auto' (a first "
+                         "chunk of 37%% of the plans, then the rest), a number of equal chunks (1 = "
+                         "one stream), or comma-separated sizes")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args(argv)
@@ -137,15 +144,29 @@ def main(argv=None) -> int:
         e.record(stream)
         return e
 
+    if args.chunks == "auto":
+        # the first chunk's planner runs under the second chunk's histogram and
+        # the second planner under the first chunk's reroute (measured optimum
+        # between 34% and 40% of the plans)
+        first = max(1, round(0.37 * P))
+        chunks = [first, P - first] if P - first >= 1 else 1
+    elif "," in args.chunks:
+        chunks = [int(x) for x in args.chunks.split(",")]
+    else:
+        chunks = int(args.chunks)
+    pipe = ep.PathPipeline(lay, P, N, chunks=chunks, device=dev) if chunks != 1 else None
     rec = dict(path=[], stats=[], fill=[])
 
     def step(record: bool):
         # events only at the ends of the path: an event between two kernels
         # leaves the GPU idle for a few microseconds
         a = ev()
-        ep.ep_load_histogram(ids, lay, load=load, ws=ws, status=status)
-        ep.ep_plan_quota(load, lay, out=plan, status=status)
-        ep.ep_reroute(ids, lay, plan.phy_quota, plan.log2phy, plan.logcnt, ws, phys_ids=phys)
+        if pipe is None:
+            ep.ep_load_histogram(ids, lay, load=load, ws=ws, status=status)
+            ep.ep_plan_quota(load, lay, out=plan, status=status)
+            ep.ep_reroute(ids, lay, plan.phy_quota, plan.log2phy, plan.logcnt, ws, phys_ids=phys)
+        else:
+            pipe.run(ids, load, status, plan, phys)
         d = ev()
         ep.ep_balance_stats(load, plan.phy_quota, lay, stats=stats, imbalance=imb, want_rank_load=False)
         f = ev()
@@ -194,6 +215,12 @@ def main(argv=None) -> int:
     ph_plan = lat(lambda: ep.ep_plan_quota(load, lay, out=plan, status=status), 10) * 1e-3
     ph_rr = lat(lambda: ep.ep_reroute(ids, lay, plan.phy_quota, plan.log2phy, plan.logcnt, ws,
                                       phys_ids=phys), 10) * 1e-3
+    # the same path as one stream of three launches, for comparison
+    def serial():
+        ep.ep_load_histogram(ids, lay, load=load, ws=ws, status=status)
+        ep.ep_plan_quota(load, lay, out=plan, status=status)
+        ep.ep_reroute(ids, lay, plan.phy_quota, plan.log2phy, plan.logcnt, ws, phys_ids=phys)
+    ph_serial = lat(serial, 10) * 1e-3
     hist_gbps = 4.0 * P * N / (ph_hist * 1e-3) / 1e9
     rr_gbps = 8.0 * P * N / (ph_rr * 1e-3) / 1e9
 
@@ -271,7 +298,9 @@ def main(argv=None) -> int:
                      "launch_ms": float(fill_ms.mean())},
         "phases_ms_per_step": {"path": path_ms, "stats": statistics.mean(ms["stats"]),
                                "fill": float(fill_ms.sum())},
-        "phases_ms_alone": {"hist": ph_hist, "plan": ph_plan, "reroute": ph_rr},
+        "phases_ms_alone": {"hist": ph_hist, "plan": ph_plan, "reroute": ph_rr,
+                            "path_one_stream": ph_serial},
+        "path_chunks": [b - a for a, b in pipe.bounds] if pipe is not None else [P],
         "kernels": {
             "hist_GBps": hist_gbps, "hist_frac": hist_gbps / HBM_PEAK_GBPS,
             "reroute_GBps": rr_gbps, "reroute_frac": rr_gbps / HBM_PEAK_GBPS,

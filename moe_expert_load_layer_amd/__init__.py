@@ -282,6 +282,80 @@ def ep_balance_stats(load: torch.Tensor, phy_quota: torch.Tensor, layout: Layout
     return stats, imbalance, rank_load
 
 
+def plan_rows(plan: PlanOut, a: int, b: int) -> PlanOut:
+    """Plans a..b-1 of a batch of plan outputs (views, no copy)."""
+    return PlanOut(plan.phy2log[a:b], plan.phy_quota[a:b], plan.logcnt[a:b], plan.log2phy[a:b],
+                   plan.steps[a:b])
+
+
+class PathPipeline:
+    """hist -> plan -> reroute over a batch of plans, cut into chunks of plans and
+    overlapped across three streams: the planner of chunk c runs while the
+    histogram of chunk c + 1 streams, and the reroute of chunk c while the planner
+    of chunk c + 1 runs.  The outputs are those of the same calls made in order
+    on one stream.  Owns its streams, events and per-chunk workspaces; the caller
+    owns inputs and outputs.  run() only enqueues: it is ordered after earlier
+    work on the caller's stream, and later work on that stream waits for it."""
+
+    def __init__(self, layout: Layout, num_plans: int, pairs_per_plan: int, chunks=2, device=None):
+        """chunks: a number of equal chunks, or the list of chunk sizes (plans).
+        The planner of a chunk takes about as long as its slowest plan, whatever
+        the chunk's size, and the planners run one after another; a first chunk
+        of about a third of the plans lets its planner run under the histogram of
+        the rest, and the second planner under the first chunk's reroute."""
+        dev = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+        if isinstance(chunks, int):
+            n = max(1, min(chunks, int(num_plans)))
+            base, extra = divmod(int(num_plans), n)
+            sizes = [base + (1 if c < extra else 0) for c in range(n)]
+        else:
+            sizes = [int(x) for x in chunks]
+        if not sizes or min(sizes) < 1 or sum(sizes) != int(num_plans):
+            raise ValueError(f"chunk sizes {sizes} do not split {num_plans} plans")
+        self.bounds = []
+        a = 0
+        for s in sizes:
+            self.bounds.append((a, a + s))
+            a += s
+        self.layout = layout
+        self.num_plans, self.pairs_per_plan = int(num_plans), int(pairs_per_plan)
+        self.ws = []
+        for a, b in self.bounds:
+            nbytes = ep_workspace_bytes(self.pairs_per_plan, b - a, layout.num_experts)
+            self.ws.append(torch.empty(max(16, nbytes), dtype=torch.uint8, device=dev))
+        # default-priority streams
+        self.s_hist, self.s_plan, self.s_rr = (torch.cuda.Stream(device=dev) for _ in range(3))
+        self.e_start, self.e_done = torch.cuda.Event(), torch.cuda.Event()
+        self.e_hist = [torch.cuda.Event() for _ in self.bounds]
+        self.e_plan = [torch.cuda.Event() for _ in self.bounds]
+
+    def run(self, topk_ids: torch.Tensor, load: torch.Tensor, status: torch.Tensor, plan: PlanOut,
+            phys_ids: torch.Tensor, stream=None):
+        if tuple(topk_ids.shape) != (self.num_plans, self.pairs_per_plan):
+            raise ValueError(f"topk_ids shape {tuple(topk_ids.shape)} != "
+                             f"({self.num_plans}, {self.pairs_per_plan})")
+        main = stream if stream is not None else torch.cuda.current_stream()
+        lay = self.layout
+        self.e_start.record(main)
+        for s in (self.s_hist, self.s_plan, self.s_rr):
+            s.wait_event(self.e_start)
+        for c, (a, b) in enumerate(self.bounds):
+            ep_load_histogram(topk_ids[a:b], lay, load=load[a:b], ws=self.ws[c], status=status[a:b],
+                              stream=self.s_hist)
+            self.e_hist[c].record(self.s_hist)
+        for c, (a, b) in enumerate(self.bounds):
+            self.s_plan.wait_event(self.e_hist[c])
+            ep_plan_quota(load[a:b], lay, out=plan_rows(plan, a, b), status=status[a:b],
+                          stream=self.s_plan)
+            self.e_plan[c].record(self.s_plan)
+        for c, (a, b) in enumerate(self.bounds):
+            self.s_rr.wait_event(self.e_plan[c])
+            ep_reroute(topk_ids[a:b], lay, plan.phy_quota[a:b], plan.log2phy[a:b], plan.logcnt[a:b],
+                       self.ws[c], phys_ids=phys_ids[a:b], stream=self.s_rr)
+        self.e_done.record(self.s_rr)
+        main.wait_event(self.e_done)
+
+
 def run_path(topk_ids: torch.Tensor, layout: Layout, stream=None):
     """hist -> plan -> reroute -> stats for a batch of plans; returns a dict of device tensors."""
     load, ws, status = ep_load_histogram(topk_ids, layout, stream=stream)

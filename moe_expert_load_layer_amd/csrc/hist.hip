@@ -100,7 +100,7 @@ __global__ __launch_bounds__(kHistWaves * kWave) void hist_kernel(
     }
 }
 
-constexpr int kScanWaves = 16;
+constexpr int kScanWaves = 4;  // small workgroups start on a CU busy with other kernels
 constexpr int kScanUnroll = 8;
 
 __global__ __launch_bounds__(kScanWaves * kWave) void scan_kernel(
