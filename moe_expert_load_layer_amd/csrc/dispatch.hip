@@ -7,45 +7,40 @@
 // position off_s + (j - Q).  With quotas that cover the loads this is the
 // stable counting sort of the pairs by physical slot.
 //
-// One wave per sub-block (the histogram's).  Every pair needs its rank among
-// the pairs of its expert, so each 64-pair group is ranked with an LDS bit
-// mask per expert (each lane ORs its bit, counts the bits below it) plus a
-// per-expert running count started from the scanned workspace row.  The block
-// lays out per instance (cumulative end, off_s - Q) so a binary search on the
-// rank gives the position directly.  Positions are unique, so the writes of
+// One wave per sub-block (the histogram's); each workgroup builds the plan's
+// route table (slot offsets, per-instance (end, off - Q)) once and its waves
+// then walk many sub-blocks.  Every pair needs its rank among the pairs of
+// its expert, so each 64-pair column is ranked with an LDS bit mask per
+// expert (each lane ORs its bit, counts the bits below it) plus a per-expert
+// running count; the first rank of the expert in the sub-block comes from the
+// histogram's workspace rows.  Positions are unique, so the writes of
 // dispatch_src never collide.
 //
-// dispatch_src is written through LDS: each wave stages the in-sub-block index
-// of every pair at (expert's offset within the sub-block + its rank k there),
-// then walks the experts in order; the pairs of one expert occupy consecutive
-// positions (one run per instance it spans), so the stores are coalesced
-// runs instead of 4-byte scatters.  Sub-blocks too large for the staging
-// buffer scatter directly.
+// dispatch_src is written through LDS when the staging buffer leaves enough
+// waves resident: each wave stages the in-sub-block index of every pair at
+// (its cell's offset + its rank), marks where each non-empty cell starts, and
+// then writes the staged slots in order, 64 at a time; a cell's pairs go to
+// consecutive positions, so each store writes a few coalesced runs.
+// Otherwise each pair's index is stored at its position directly.
 #include "ep_internal.h"
 
 namespace ep {
 namespace {
 
-// Per-expert state of a wave's sub-block: ranks come from the bit mask of the
-// current 64-pair group plus the count of earlier groups.
-struct CellState {
+// Per-expert state of a wave's sub-block (16 bytes): the bit mask of the
+// current 64-pair column, the count of the expert's pairs in earlier columns
+// with two flags in its top bits, and the position base: run + (off - Q) of
+// the one instance that takes all of the expert's pairs here, or the run
+// itself when a quota boundary falls inside (split), so that the k-th pair
+// of the cell goes to base + k, or to the instance a search of run + k finds.
+struct Cell {
     uint64_t mask;
-    int32_t k;     // pairs of the expert seen so far in this sub-block
-    int32_t off;   // staging offset of the expert's pairs (staged layout)
+    uint32_t kf;
+    int32_t base;
 };
-
-// Where an expert's pairs of one sub-block go: staging offset, first rank,
-// count, and the position shift of the one instance that takes all of them
-// (kSplitCell if they cross a quota boundary, kNoCell if none is placed).
-struct CellInfo {
-    int32_t off;
-    int32_t run;
-    int32_t cnt;
-    int32_t delta;
-};
-
-constexpr int32_t kSplitCell = (int32_t)0x80000000;
-constexpr int32_t kNoCell = (int32_t)0x80000001;
+constexpr uint32_t kSplitFlag = 1u << 30;  // a quota boundary falls inside the cell
+constexpr uint32_t kNoneFlag = 1u << 31;   // no instance takes these pairs
+constexpr uint32_t kCountMask = kSplitFlag - 1;
 
 __device__ __forceinline__ int32_t position_of(const int2 *inst, int f, int n, int32_t j) {
     int lo = 0, hi = n;
@@ -64,13 +59,16 @@ __global__ __launch_bounds__(W *kWave) void dispatch_kernel(
     const int32_t *__restrict__ log2phy, const int32_t *__restrict__ logcnt,
     int32_t *__restrict__ slot_offsets, int32_t *__restrict__ dpos, int32_t *__restrict__ dsrc) {
     extern __shared__ __align__(16) unsigned char sh_raw[];
-    CellState *st_all = reinterpret_cast<CellState *>(sh_raw);             // [W][E]
-    CellInfo *ci_all = reinterpret_cast<CellInfo *>(st_all + (size_t)W * E); // [W][E]
-    int2 *inst = reinterpret_cast<int2 *>(ci_all + (size_t)W * E);          // [Phi] (end, off - Q)
+    const int64_t nwords = STAGED ? sub / kWave : 0;                         // cell-start bit words
+    Cell *cell_all = reinterpret_cast<Cell *>(sh_raw);                      // [W][E]
+    uint64_t *sbits_all = reinterpret_cast<uint64_t *>(cell_all + (size_t)W * E); // [W][sub/64] if STAGED
+    int2 *inst = reinterpret_cast<int2 *>(sbits_all + (size_t)W * nwords);  // [Phi] (end, off - Q)
     int32_t *soff = reinterpret_cast<int32_t *>(inst + Phi);                // [Phi + 1]
     int32_t *rfirst = soff + Phi + 1;                                       // [E]
     int32_t *rcnt = rfirst + E;                                             // [E]
-    uint16_t *stage_all = reinterpret_cast<uint16_t *>(rcnt + E);           // [W][sub] if STAGED
+    int32_t *nel_all = rcnt + E;                                            // [W][E] if STAGED
+    int32_t *off_all = nel_all + (STAGED ? (size_t)W * E : 0);              // [W][E] if STAGED
+    uint16_t *stage_all = reinterpret_cast<uint16_t *>(off_all + (STAGED ? (size_t)W * E : 0)); // [W][sub]
     const int wave = threadIdx.x / kWave;
     const int lane = threadIdx.x % kWave;
     const int p = blockIdx.y;
@@ -124,17 +122,27 @@ __global__ __launch_bounds__(W *kWave) void dispatch_kernel(
         for (int s = threadIdx.x; s <= Phi; s += W * kWave) slot_offsets[(int64_t)p * (Phi + 1) + s] = soff[s];
     __syncthreads();
 
-    const int64_t sb = (int64_t)blockIdx.x * W + wave;
-    if (sb >= nsb) return;  // per-wave state below: no more block barriers
-    CellState *st = st_all + (size_t)wave * E;
-    CellInfo *ci = ci_all + (size_t)wave * E;
+    // each wave walks the plan's sub-blocks with a stride of the plan's waves,
+    // reusing the block's route table; no block barriers below
+    for (int64_t sb = (int64_t)blockIdx.x * W + wave; sb < nsb; sb += (int64_t)gridDim.x * W) {
+    wave_lds_fence();  // the previous sub-block's reads of the wave's LDS are done
+    Cell *cells = cell_all + (size_t)wave * E;
+    int32_t *offs = off_all + (size_t)wave * (STAGED ? E : 0);  // staging offset of each cell
     uint16_t *stage = stage_all + (size_t)wave * (STAGED ? sub : 0);
+    uint64_t *sbits = sbits_all + (size_t)wave * nwords;   // bit t: staged slot t starts a cell
+    int32_t *nel = nel_all + (size_t)wave * (STAGED ? E : 0);  // non-empty cells' experts, in order
     const SubPrefix pre = sub_prefix(ws, p, sb, nsb, sps, nseg, E1);
+    int staged_pairs = 0;
+    if (STAGED) {
+        for (int64_t w = lane; w < nwords; w += kWave) sbits[w] = 0ull;
+        wave_lds_fence();
+    }
     {
-        int carry = 0;
+        int carry = 0, ncells = 0;
         for (int c = 0; c < E; c += kWave) {
             const int e = c + lane;
-            int32_t run = 0, cnt = 0, delta = kNoCell;
+            int32_t run = 0, cnt = 0, base = 0;
+            uint32_t flags = kNoneFlag;
             if (e < E) {
                 run = pre.start(e);
                 cnt = pre.end(e) - run;
@@ -144,18 +152,37 @@ __global__ __launch_bounds__(W *kWave) void dispatch_kernel(
                     const int mid = (lo + hi) >> 1;
                     if (run < inst[f + mid].x) hi = mid; else lo = mid + 1;
                 }
-                if (cnt > 0 && lo < n && inst[f + lo].y != (int32_t)0x80000000)
-                    delta = run + cnt <= inst[f + lo].x ? inst[f + lo].y : kSplitCell;
-                else if (cnt > 0 && lo < n)
-                    delta = kSplitCell;
+                base = run;
+                if (cnt > 0 && lo < n && inst[f + lo].y != (int32_t)0x80000000) {
+                    if (run + cnt <= inst[f + lo].x) {
+                        flags = 0;
+                        base = run + inst[f + lo].y;
+                    } else {
+                        flags = kSplitFlag;
+                    }
+                } else if (cnt > 0 && lo < n) {
+                    flags = kSplitFlag;
+                }
             }
             const int incl = wave_incl_scan_i32(cnt);
+            const int off = carry + incl - cnt;
             if (e < E) {
-                ci[e] = CellInfo{carry + incl - cnt, run, cnt, delta};
-                st[e] = CellState{0ull, 0, carry + incl - cnt};
+                cells[e] = Cell{0ull, flags, base};
+                if (STAGED) offs[e] = off;
+            }
+            if (STAGED) {
+                const bool full = e < E && cnt > 0;
+                const uint64_t fm = __ballot(full);
+                if (full) {
+                    nel[ncells + __popcll(fm & lanemask_lt())] = e;
+                    atomicOr(reinterpret_cast<unsigned long long *>(&sbits[off / kWave]),
+                             1ull << (off % kWave));
+                }
+                ncells += __popcll(fm);
             }
             carry += __shfl(incl, kWave - 1);
         }
+        staged_pairs = carry;
     }
     wave_lds_fence();
 
@@ -168,33 +195,43 @@ __global__ __launch_bounds__(W *kWave) void dispatch_kernel(
     const uint64_t bit = 1ull << lane;
     const uint32_t uE = (uint32_t)E;
     constexpr int U = 8;
+    // the IDs of the next U columns load while the current ones are ranked
+    int32_t nxt[U];
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+        const int64_t i = begin + u * kWave + lane;
+        nxt[u] = i < end ? __builtin_nontemporal_load(src + i) : -1;
+    }
     for (int64_t g = begin; g < end; g += U * kWave) {
         int32_t v[U];
 #pragma unroll
         for (int u = 0; u < U; u++) {
-            const int64_t i = g + u * kWave + lane;
-            v[u] = i < end ? __builtin_nontemporal_load(src + i) : -1;
+            v[u] = nxt[u];
+            const int64_t i = g + (U + u) * kWave + lane;
+            nxt[u] = i < end ? __builtin_nontemporal_load(src + i) : -1;
         }
 #pragma unroll
         for (int u = 0; u < U; u++) {
             const int32_t x = v[u];
             const bool valid = (uint32_t)x < uE;
-            if (valid) atomicOr(reinterpret_cast<unsigned long long *>(&st[x].mask), bit);
+            if (valid) atomicOr(reinterpret_cast<unsigned long long *>(&cells[x].mask), bit);
             wave_lds_fence();
-            CellState cur{0ull, 0, 0};
-            if (valid) cur = st[x];
+            Cell cur{0ull, 0u, 0};
+            int32_t off = 0;
+            if (valid) {
+                cur = cells[x];
+                if (STAGED) off = offs[x];
+            }
             wave_lds_fence();
             const int64_t i = g + u * kWave + lane;
             int32_t pos = -1;
             if (valid) {
                 const uint64_t below = cur.mask & lt;
-                if (below == 0) st[x] = CellState{0ull, cur.k + (int32_t)__popcll(cur.mask), cur.off};
-                const int32_t k = cur.k + (int32_t)__popcll(below);
-                const CellInfo cell = ci[x];
-                const int32_t j = cell.run + k;
-                if (cell.delta == kSplitCell) pos = position_of(inst, rfirst[x], rcnt[x], j);
-                else if (cell.delta != kNoCell) pos = j + cell.delta;
-                if (STAGED) stage[cur.off + k] = (uint16_t)(i - begin);
+                if (below == 0) cells[x] = Cell{0ull, cur.kf + (uint32_t)__popcll(cur.mask), cur.base};
+                const int32_t k = (int32_t)(cur.kf & kCountMask) + (int32_t)__popcll(below);
+                if (cur.kf & kSplitFlag) pos = position_of(inst, rfirst[x], rcnt[x], cur.base + k);
+                else if (!(cur.kf & kNoneFlag)) pos = cur.base + k;
+                if (STAGED) stage[off + k] = (uint16_t)(i - begin);
                 else if (pos >= 0 && pos < N) src_out[pos] = (int32_t)i;
             }
             if (i < end) pos_out[i] = pos;
@@ -202,25 +239,44 @@ __global__ __launch_bounds__(W *kWave) void dispatch_kernel(
         }
     }
     if (STAGED) {
-        // experts in order, 64 at a time: each expert's staged pairs go to
-        // consecutive positions (per instance), written as coalesced runs
-        for (int c = 0; c < E; c += kWave) {
-            const int e = c + lane;
-            CellInfo mine{0, 0, 0, kNoCell};
-            if (e < E) mine = ci[e];
-            const int last = (E - c) < kWave ? E - c : kWave;
-            for (int l = 0; l < last; l++) {
-                const int32_t cnt = __builtin_amdgcn_readlane(mine.cnt, l);
-                const int32_t delta = __builtin_amdgcn_readlane(mine.delta, l);
-                if (cnt == 0 || delta == kNoCell) continue;
-                const int32_t off = __builtin_amdgcn_readlane(mine.off, l);
-                const int32_t run = __builtin_amdgcn_readlane(mine.run, l);
-                for (int32_t t = lane; t < cnt; t += kWave) {
-                    const int32_t j = run + t;
+        // staged slots in order, 64 per step: slot t belongs to the non-empty
+        // cell whose start is the last one at or before t; each expert's
+        // slots go to consecutive positions (per instance), so every store
+        // writes a few coalesced runs
+        constexpr int UF = 4;  // windows per step: their LDS reads overlap
+        const uint64_t upto = lane == kWave - 1 ? ~0ull : ((2ull << lane) - 1);
+        int cbase = -1;  // cells started before the current window, minus one
+        for (int w0 = 0; w0 < staged_pairs; w0 += UF * kWave) {
+            uint64_t word[UF];
+            int cb[UF];
+#pragma unroll
+            for (int u = 0; u < UF; u++) {
+                const int64_t wi = w0 / kWave + u;
+                word[u] = wi < nwords ? sbits[wi] : 0ull;
+            }
+#pragma unroll
+            for (int u = 0; u < UF; u++) {
+                cb[u] = cbase;
+                cbase += __popcll(word[u]);
+            }
+            int e[UF];
+            uint16_t sidx[UF];
+#pragma unroll
+            for (int u = 0; u < UF; u++) {
+                const int t = w0 + u * kWave + lane;
+                e[u] = t < staged_pairs ? nel[cb[u] + __popcll(word[u] & upto)] : 0;
+                sidx[u] = t < staged_pairs ? stage[t] : 0;
+            }
+#pragma unroll
+            for (int u = 0; u < UF; u++) {
+                const int t = w0 + u * kWave + lane;
+                if (t < staged_pairs) {
+                    const Cell cell = cells[e[u]];
+                    const int32_t k = t - offs[e[u]];
                     int32_t pos = -1;
-                    if (delta == kSplitCell) pos = position_of(inst, rfirst[c + l], rcnt[c + l], j);
-                    else if (delta != kNoCell) pos = j + delta;
-                    if (pos >= 0 && pos < N) src_out[pos] = (int32_t)(begin + stage[off + t]);
+                    if (cell.kf & kSplitFlag) pos = position_of(inst, rfirst[e[u]], rcnt[e[u]], cell.base + k);
+                    else if (!(cell.kf & kNoneFlag)) pos = cell.base + k;
+                    if (pos >= 0 && pos < N) src_out[pos] = (int32_t)(begin + sidx[u]);
                 }
             }
         }
@@ -228,6 +284,7 @@ __global__ __launch_bounds__(W *kWave) void dispatch_kernel(
     // positions past the plan's total quota hold no pair
     const int64_t tail = soff[Phi] > begin ? soff[Phi] : begin;
     for (int64_t i = tail + lane; i < end; i += kWave) src_out[i] = -1;
+    }
 }
 
 int pick_dispatch_waves(int E, int Phi, int64_t stage) {
@@ -239,8 +296,34 @@ int pick_dispatch_waves(int E, int Phi, int64_t stage) {
 }  // namespace
 
 size_t dispatch_lds_bytes(int E, int Phi, int waves, int64_t stage_pairs) {
-    return (size_t)waves * E * (sizeof(CellState) + sizeof(CellInfo)) + (size_t)Phi * 8 +
-           (size_t)(Phi + 1) * 4 + (size_t)E * 8 + (size_t)waves * stage_pairs * 2;
+    const size_t staged = stage_pairs > 0 ? (size_t)waves * ((size_t)stage_pairs / kWave * 8 + (size_t)E * 8 +
+                                                             (size_t)stage_pairs * 2)
+                                          : 0;
+    return (size_t)waves * E * sizeof(Cell) + (size_t)Phi * 8 +
+           (size_t)(Phi + 1) * 4 + (size_t)E * 8 + staged;
+}
+
+// blocks of dispatch_kernel<w, staged> the device holds at once (0 if unknown)
+static int resident_blocks(int w, bool staged, size_t lds) {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+        (void)hipGetLastError();  // clear it: the launch below reports its own
+        return 0;
+    }
+    const void *fn = nullptr;
+    if (staged) {
+        fn = w == 4 ? (const void *)dispatch_kernel<4, true>
+                    : w == 2 ? (const void *)dispatch_kernel<2, true> : (const void *)dispatch_kernel<1, true>;
+    } else {
+        fn = w == 4 ? (const void *)dispatch_kernel<4, false>
+                    : w == 2 ? (const void *)dispatch_kernel<2, false> : (const void *)dispatch_kernel<1, false>;
+    }
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, w * kWave, lds) != hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    return cus * per_cu;
 }
 
 hipError_t launch_dispatch(const int32_t *ids, int64_t N, int32_t P, const ep_layout_t &L,
@@ -249,14 +332,47 @@ hipError_t launch_dispatch(const int32_t *ids, int64_t N, int32_t P, const ep_la
                            int32_t *dpos, int32_t *dsrc, hipStream_t s) {
     const int64_t sub = g.sub, nsb = g.nsb, sps = g.sps, nseg = g.nseg;
     const int E = L.num_experts, Phi = L.num_phys, rho = L.max_replicas;
-    // stage through LDS when a sub-block's pair indices fit (16-bit, 1 or 2 waves)
-    int w = sub <= 65536 ? pick_dispatch_waves(E, Phi, sub) : 0;
-    const bool staged = w > 0;
-    if (!staged) w = pick_dispatch_waves(E, Phi, 0);
+    // stage through LDS when a sub-block's pair indices fit (16-bit); of the
+    // wave counts whose LDS fits a workgroup, take the one with the most
+    // resident waves (the kernel is bound by LDS latency, so occupancy counts)
+    // Staging turns the scatter of dispatch_src into runs, but its buffer
+    // (2 bytes per pair of a sub-block) lowers occupancy; below 8 resident
+    // waves per CU the direct scatter is faster.
+    int cus = 0, dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+        (void)hipGetLastError();
+        cus = 0;
+    }
+    auto best_waves = [&](bool st, int &w_out) {
+        const int w0 = pick_dispatch_waves(E, Phi, st ? sub : 0);
+        int best = w0, waves = -1;
+        for (int c = w0; c >= 1; c >>= 1) {
+            const int r = resident_blocks(c, st, dispatch_lds_bytes(E, Phi, c, st ? sub : 0));
+            if (r * c > waves) { best = c; waves = r * c; }
+        }
+        w_out = w0 > 0 ? best : 0;
+        return w0 > 0 ? waves : -1;
+    };
+    int w = 0, wu = 0;
+    const int ws_waves = sub <= 65536 ? best_waves(true, w) : -1;
+    bool staged = ws_waves >= 0 && w > 0;
+    if (!staged || (cus > 0 && ws_waves < 8 * cus)) {
+        const int wu_waves = best_waves(false, wu);
+        if (wu > 0 && (!staged || wu_waves > ws_waves)) { staged = false; w = wu; }
+    }
     if (w == 0) return hipErrorInvalidValue;
     const size_t lds = dispatch_lds_bytes(E, Phi, w, staged ? sub : 0);
-    // at least one block per plan so the slot offsets are always written
-    const int64_t nblk = nsb > 0 ? (nsb + w - 1) / w : 1;
+    // Blocks per plan: every block builds the plan's route table once, so a
+    // launch of many plans uses no more blocks than the GPU holds at once
+    // (one round, equal work), each wave walking many sub-blocks.  At least one
+    // block per plan, so the slot offsets are always written.
+    int64_t nblk = nsb > 0 ? (nsb + w - 1) / w : 1;
+    const int resident = resident_blocks(w, staged, lds);
+    if (resident > 0) {
+        const int64_t per_plan = resident / P > 0 ? resident / P : 1;
+        if (per_plan < nblk) nblk = per_plan;
+    }
     dim3 grid((unsigned)nblk, (unsigned)P);
 #define EP_DISPATCH(WV, ST)                                                                        \
     hipLaunchKernelGGL((dispatch_kernel<WV, ST>), grid, dim3(WV * kWave), lds, s, ids, N, E, Phi, rho, \
