@@ -60,15 +60,17 @@ __global__ __launch_bounds__(W *kWave) void dispatch_kernel(
     int32_t *__restrict__ slot_offsets, int32_t *__restrict__ dpos, int32_t *__restrict__ dsrc) {
     extern __shared__ __align__(16) unsigned char sh_raw[];
     const int64_t nwords = STAGED ? sub / kWave : 0;                         // cell-start bit words
-    Cell *cell_all = reinterpret_cast<Cell *>(sh_raw);                      // [W][E]
-    uint64_t *sbits_all = reinterpret_cast<uint64_t *>(cell_all + (size_t)W * E); // [W][sub/64] if STAGED
+    const int E1c = E + 1;                                                  // cell E: padding, bad IDs
+    const int64_t sstride = STAGED ? sub + kWave : 0;                       // slot sub: sink
+    Cell *cell_all = reinterpret_cast<Cell *>(sh_raw);                      // [W][E+1]
+    uint64_t *sbits_all = reinterpret_cast<uint64_t *>(cell_all + (size_t)W * E1c); // [W][sub/64] if STAGED
     int2 *inst = reinterpret_cast<int2 *>(sbits_all + (size_t)W * nwords);  // [Phi] (end, off - Q)
     int32_t *soff = reinterpret_cast<int32_t *>(inst + Phi);                // [Phi + 1]
     int32_t *rfirst = soff + Phi + 1;                                       // [E]
     int32_t *rcnt = rfirst + E;                                             // [E]
     int32_t *nel_all = rcnt + E;                                            // [W][E] if STAGED
     int32_t *off_all = nel_all + (STAGED ? (size_t)W * E : 0);              // [W][E] if STAGED
-    uint16_t *stage_all = reinterpret_cast<uint16_t *>(off_all + (STAGED ? (size_t)W * E : 0)); // [W][sub]
+    uint16_t *stage_all = reinterpret_cast<uint16_t *>(off_all + (STAGED ? (size_t)W * E : 0)); // [W][sub + 64]
     const int wave = threadIdx.x / kWave;
     const int lane = threadIdx.x % kWave;
     const int p = blockIdx.y;
@@ -126,9 +128,9 @@ __global__ __launch_bounds__(W *kWave) void dispatch_kernel(
     // reusing the block's route table; no block barriers below
     for (int64_t sb = (int64_t)blockIdx.x * W + wave; sb < nsb; sb += (int64_t)gridDim.x * W) {
     wave_lds_fence();  // the previous sub-block's reads of the wave's LDS are done
-    Cell *cells = cell_all + (size_t)wave * E;
+    Cell *cells = cell_all + (size_t)wave * E1c;
     int32_t *offs = off_all + (size_t)wave * (STAGED ? E : 0);  // staging offset of each cell
-    uint16_t *stage = stage_all + (size_t)wave * (STAGED ? sub : 0);
+    uint16_t *stage = stage_all + (size_t)wave * sstride;
     uint64_t *sbits = sbits_all + (size_t)wave * nwords;   // bit t: staged slot t starts a cell
     int32_t *nel = nel_all + (size_t)wave * (STAGED ? E : 0);  // non-empty cells' experts, in order
     const SubPrefix pre = sub_prefix(ws, p, sb, nsb, sps, nseg, E1);
@@ -183,6 +185,7 @@ __global__ __launch_bounds__(W *kWave) void dispatch_kernel(
             carry += __shfl(incl, kWave - 1);
         }
         staged_pairs = carry;
+        if (lane == 0) cells[E] = Cell{0ull, kNoneFlag, 0};
     }
     wave_lds_fence();
 
@@ -214,26 +217,20 @@ __global__ __launch_bounds__(W *kWave) void dispatch_kernel(
         for (int u = 0; u < U; u++) {
             const int32_t x = v[u];
             const bool valid = (uint32_t)x < uE;
-            if (valid) atomicOr(reinterpret_cast<unsigned long long *>(&cells[x].mask), bit);
+            const int xi = valid ? x : E;  // padding and bad IDs rank in the sink cell
+            atomicOr(reinterpret_cast<unsigned long long *>(&cells[xi].mask), bit);
             wave_lds_fence();
-            Cell cur{0ull, 0u, 0};
-            int32_t off = 0;
-            if (valid) {
-                cur = cells[x];
-                if (STAGED) off = offs[x];
-            }
+            const Cell cur = cells[xi];
+            const int32_t off = STAGED && valid ? offs[xi] : 0;
             wave_lds_fence();
             const int64_t i = g + u * kWave + lane;
-            int32_t pos = -1;
-            if (valid) {
-                const uint64_t below = cur.mask & lt;
-                if (below == 0) cells[x] = Cell{0ull, cur.kf + (uint32_t)__popcll(cur.mask), cur.base};
-                const int32_t k = (int32_t)(cur.kf & kCountMask) + (int32_t)__popcll(below);
-                if (cur.kf & kSplitFlag) pos = position_of(inst, rfirst[x], rcnt[x], cur.base + k);
-                else if (!(cur.kf & kNoneFlag)) pos = cur.base + k;
-                if (STAGED) stage[off + k] = (uint16_t)(i - begin);
-                else if (pos >= 0 && pos < N) src_out[pos] = (int32_t)i;
-            }
+            const uint64_t below = cur.mask & lt;
+            if (below == 0) cells[xi] = Cell{0ull, cur.kf + (uint32_t)__popcll(cur.mask), cur.base};
+            const int32_t k = (int32_t)(cur.kf & kCountMask) + (int32_t)__popcll(below);
+            int32_t pos = (cur.kf & (kNoneFlag | kSplitFlag)) ? -1 : cur.base + k;
+            if (cur.kf & kSplitFlag) pos = position_of(inst, rfirst[xi], rcnt[xi], cur.base + k);
+            if (STAGED) stage[valid ? off + k : sub] = (uint16_t)(i - begin);
+            else if (pos >= 0 && pos < N) src_out[pos] = (int32_t)i;
             if (i < end) pos_out[i] = pos;
             wave_lds_fence();
         }
@@ -297,9 +294,9 @@ int pick_dispatch_waves(int E, int Phi, int64_t stage) {
 
 size_t dispatch_lds_bytes(int E, int Phi, int waves, int64_t stage_pairs) {
     const size_t staged = stage_pairs > 0 ? (size_t)waves * ((size_t)stage_pairs / kWave * 8 + (size_t)E * 8 +
-                                                             (size_t)stage_pairs * 2)
+                                                             ((size_t)stage_pairs + kWave) * 2)
                                           : 0;
-    return (size_t)waves * E * sizeof(Cell) + (size_t)Phi * 8 +
+    return (size_t)waves * (E + 1) * sizeof(Cell) + (size_t)Phi * 8 +
            (size_t)(Phi + 1) * 4 + (size_t)E * 8 + staged;
 }
 
