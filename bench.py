@@ -89,9 +89,10 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work (0 = skip)")
     ap.add_argument("--latency-reps", type=int, default=30)
     ap.add_argument("--chunks", default="auto",
-                    help="plans per step cut into chunks overlapped across streams: 'auto' (a first "
-                         "chunk of 37%% of the plans, then the rest), a number of equal chunks (1 = "
-                         "one stream), or comma-separated sizes")
+                    help="plans per step cut into chunks overlapped across streams: 'auto' (the "
+                         "fastest of one stream and a first chunk of 25/37/50%% of the plans, timed "
+                         "during warmup), a number of equal chunks (1 = one stream), or "
+                         "comma-separated sizes")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args(argv)
@@ -144,29 +145,56 @@ def main(argv=None) -> int:
         e.record(stream)
         return e
 
+    def run_chunks(c):
+        return ep.PathPipeline(lay, P, N, chunks=c, device=dev) if c != 1 else None
+
+    def path_once(pp):
+        if pp is None:
+            ep.ep_load_histogram(ids, lay, load=load, ws=ws, status=status)
+            ep.ep_plan_quota(load, lay, out=plan, status=status)
+            ep.ep_reroute(ids, lay, plan.phy_quota, plan.log2phy, plan.logcnt, ws, phys_ids=phys)
+        else:
+            pp.run(ids, load, status, plan, phys)
+
+    tuning = None
     if args.chunks == "auto":
-        # the first chunk's planner runs under the second chunk's histogram and
-        # the second planner under the first chunk's reroute (measured optimum
-        # between 34% and 40% of the plans)
-        first = max(1, round(0.37 * P))
-        chunks = [first, P - first] if P - first >= 1 else 1
+        # A planner launch takes about as long as its slowest plan; overlapping
+        # it with another chunk's streaming kernels pays only when that chunk
+        # streams for at least as long.  Pick among one stream and a first
+        # chunk of 25 / 37 / 50 % of the plans by timing each on this workload
+        # (part of the warmup, outside the timed steps).
+        cands = [1] + sorted({(f, P - f) for f in (round(0.25 * P), round(0.37 * P), round(0.5 * P))
+                              if 1 <= f < P})
+        tuning = {}
+        best, best_ms = 1, None
+        for c in cands:
+            cc = list(c) if c != 1 else 1
+            pp = run_chunks(cc)
+            path_once(pp)
+            xs = []
+            for _ in range(3):
+                a = torch.cuda.Event(enable_timing=True); b = torch.cuda.Event(enable_timing=True)
+                a.record(stream); path_once(pp); b.record(stream)
+                xs.append((a, b))
+            torch.cuda.synchronize()
+            t_ms = statistics.median(_elapsed(xs))
+            tuning["one stream" if cc == 1 else ",".join(map(str, cc))] = t_ms
+            if best_ms is None or t_ms < best_ms:
+                best, best_ms = cc, t_ms
+            del pp
+        chunks = best
     elif "," in args.chunks:
         chunks = [int(x) for x in args.chunks.split(",")]
     else:
         chunks = int(args.chunks)
-    pipe = ep.PathPipeline(lay, P, N, chunks=chunks, device=dev) if chunks != 1 else None
+    pipe = run_chunks(chunks)
     rec = dict(path=[], stats=[], fill=[])
 
     def step(record: bool):
         # events only at the ends of the path: an event between two kernels
         # leaves the GPU idle for a few microseconds
         a = ev()
-        if pipe is None:
-            ep.ep_load_histogram(ids, lay, load=load, ws=ws, status=status)
-            ep.ep_plan_quota(load, lay, out=plan, status=status)
-            ep.ep_reroute(ids, lay, plan.phy_quota, plan.log2phy, plan.logcnt, ws, phys_ids=phys)
-        else:
-            pipe.run(ids, load, status, plan, phys)
+        path_once(pipe)
         d = ev()
         ep.ep_balance_stats(load, plan.phy_quota, lay, stats=stats, imbalance=imb, want_rank_load=False)
         f = ev()
@@ -301,6 +329,7 @@ def main(argv=None) -> int:
         "phases_ms_alone": {"hist": ph_hist, "plan": ph_plan, "reroute": ph_rr,
                             "path_one_stream": ph_serial},
         "path_chunks": [b - a for a, b in pipe.bounds] if pipe is not None else [P],
+        "path_chunk_tuning_ms": tuning,
         "kernels": {
             "hist_GBps": hist_gbps, "hist_frac": hist_gbps / HBM_PEAK_GBPS,
             "reroute_GBps": rr_gbps, "reroute_frac": rr_gbps / HBM_PEAK_GBPS,
@@ -331,6 +360,20 @@ def main(argv=None) -> int:
             ok &= np.array_equal(phys[p].cpu().numpy(), ph)
         out["cpu_baseline"] = cb
         out["parity_on_cpu_sample"] = bool(ok)
+        # slot-count lower bound on the maximum rank load of the same layers
+        # (no plan can beat it), as an imbalance, beside the planner's result
+        from oracle.brute import slot_lower_bound
+        lbs = []
+        for p, (ld, _, _) in enumerate(outs):
+            tot = int(ld.sum())
+            if tot > 0:
+                lam = slot_lower_bound(ld, wl.num_ranks, wl.num_spare)
+                lbs.append((lam * wl.num_ranks / tot, float(imb_np[p, 1])))
+        if lbs:
+            lb = np.array(lbs)
+            out["balance"]["lower_bound_layers"] = len(lbs)
+            out["balance"]["imbalance_lower_bound_mean"] = float(lb[:, 0].mean())
+            out["balance"]["imbalance_after_over_bound_max"] = float((lb[:, 1] / lb[:, 0]).max())
         cb["host_threads_available"] = os.cpu_count()
     else:
         out["cpu_baseline"] = None
