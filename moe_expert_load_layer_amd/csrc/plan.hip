@@ -293,6 +293,11 @@ __global__ __launch_bounds__(kWave) void plan_kernel_lanes(const int32_t *__rest
     extern __shared__ __align__(16) unsigned char sh_raw[];
     uint64_t *emask = reinterpret_cast<uint64_t *>(sh_raw);      // [E] ranks of live replicas
     int32_t *nri = reinterpret_cast<int32_t *>(emask + E);       // [E] native rank << 8 | index
+    // [E] set when a move of another expert changed the load of a rank that
+    // hosts this expert after the expert was last water-filled; re-levelling
+    // an expert that is not set would reproduce its current quotas, so such
+    // candidates are skipped
+    int32_t *edirty = nri + E;
 
     const int p = blockIdx.x;
     const int lane = threadIdx.x;
@@ -303,11 +308,6 @@ __global__ __launch_bounds__(kWave) void plan_kernel_lanes(const int32_t *__rest
     const int nat = is_rank ? a.T.rank_nat[lane] : 0;
     const int spc = is_rank ? a.T.rank_first[lane + 1] - f0 - nat : 0;
     int freec = spc;
-    // bit i: native i, bit NPR + j: spare j of this rank.  Set when another
-    // expert's move changed this rank's load after the slot's expert was last
-    // water-filled; a re-level of an expert whose slots are all clean would
-    // reproduce its current quotas, so it is skipped.
-    uint32_t dirty = 0;
     int32_t nat_e[NPR], nat_ld[NPR], nat_q[NPR], nat_ic[NPR];
     int32_t sp_owner[SPR], sp_q[SPR];
 #pragma unroll
@@ -321,7 +321,7 @@ __global__ __launch_bounds__(kWave) void plan_kernel_lanes(const int32_t *__rest
     }
 #pragma unroll
     for (int j = 0; j < SPR; j++) { sp_owner[j] = -1; sp_q[j] = 0; }
-    for (int e = lane; e < E; e += kWave) emask[e] = 0;
+    for (int e = lane; e < E; e += kWave) { emask[e] = 0; edirty[e] = 0; }
     int rl = 0;
 #pragma unroll
     for (int i = 0; i < NPR; i++) rl += nat_ld[i];
@@ -363,12 +363,14 @@ __global__ __launch_bounds__(kWave) void plan_kernel_lanes(const int32_t *__rest
             crank += kj > key ? 1 : 0;
         }
         const int nc = __popcll(vm);
+        // candidates worth a re-level: replicated and set in edirty
+        const uint64_t relevel = __ballot(valid && cic >= 2 && edirty[valid ? ce : 0] != 0);
 
         bool committed = false;
-        for (int pass = 0; pass < 2 && !committed; pass++) {
+        for (int pass = relevel ? 0 : 1; pass < 2 && !committed; pass++) {
             for (int c = 0; c < nc && !committed; c++) {
                 const int cl = __ffsll((long long)__ballot(valid && crank == c)) - 1;
-                if (pass == 0 && __builtin_amdgcn_readlane(cic, cl) < 2) continue;
+                if (pass == 0 && !((relevel >> cl) & 1)) continue;
                 const int e = __builtin_amdgcn_readlane(ce, cl);
                 int nr = __builtin_amdgcn_readlane(cnr, cl);
                 int idx, T;
@@ -395,8 +397,6 @@ __global__ __launch_bounds__(kWave) void plan_kernel_lanes(const int32_t *__rest
                     if (j == jr) q = sp_q[j];
                 if (nat_here) q = pick(nat_q, idx);
                 const bool inst = nat_here || jr >= 0;
-                const uint32_t mine = (nat_here ? 1u << idx : 0u) | (jr >= 0 ? 1u << (NPR + jr) : 0u);
-                if (!replicate && !__ballot((dirty & mine) != 0)) continue;
                 const int b = rl - q;
                 bool isnew = false;
                 if (replicate) {
@@ -431,10 +431,7 @@ __global__ __launch_bounds__(kWave) void plan_kernel_lanes(const int32_t *__rest
                 const int newLh = __builtin_amdgcn_readlane(act ? b + qn : rl, h);
                 if (newLh >= Lh) continue;
                 // commit (lane-local)
-                if (act) {
-                    rl = b + qn;
-                    dirty = ~0u;
-                }
+                if (act) rl = b + qn;
                 if (nat_here) {
 #pragma unroll
                     for (int i = 0; i < NPR; i++)
@@ -448,10 +445,20 @@ __global__ __launch_bounds__(kWave) void plan_kernel_lanes(const int32_t *__rest
 #pragma unroll
                     for (int j = 0; j < SPR; j++)
                         if (j == jn) { sp_owner[j] = e; sp_q[j] = qn; }
-                    dirty &= ~(1u << (NPR + jn));
                     freec -= 1;
                 }
-                if (act) dirty &= ~mine;
+                // every expert on a rank whose load moved needs a new level,
+                // except the one just levelled
+                if (act) {
+#pragma unroll
+                    for (int i = 0; i < NPR; i++)
+                        if (i < nat) edirty[nat_e[i]] = 1;
+#pragma unroll
+                    for (int j = 0; j < SPR; j++)
+                        if (j < spc && sp_owner[j] >= 0) edirty[sp_owner[j]] = 1;
+                }
+                wave_lds_fence();
+                if (lane == 0) edirty[e] = 0;
                 committed = true;
             }
         }
@@ -512,7 +519,7 @@ size_t plan_lds_bytes(const ep_layout_t &L) {
     return 8 * E + 8 * kWave + 4 * (5 * R + 1 + 3 * Phi + 5 * E + S + kWave);
 }
 
-static size_t lanes_lds_bytes(const ep_layout_t &L) { return (size_t)L.num_experts * 12; }
+static size_t lanes_lds_bytes(const ep_layout_t &L) { return (size_t)L.num_experts * 16; }
 
 static int pow2_at_least(int x) {
     int v = 1;
