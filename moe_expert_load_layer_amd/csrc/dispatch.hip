@@ -22,8 +22,6 @@
 // then writes the staged slots in order, 64 at a time; a cell's pairs go to
 // consecutive positions, so each store writes a few coalesced runs.
 // Otherwise each pair's index is stored at its position directly.
-#include <mutex>
-
 #include "ep_internal.h"
 
 namespace ep {
@@ -302,60 +300,16 @@ size_t dispatch_lds_bytes(int E, int Phi, int waves, int64_t stage_pairs) {
            (size_t)(Phi + 1) * 4 + (size_t)E * 8 + staged;
 }
 
-// Resident workgroups of dispatch_kernel<w, staged> with `lds` bytes of LDS
-// on the current device, and its CU count (0 if unknown).  Queried once per
-// (device, shape) and cached: the launch path then costs no runtime queries.
-struct OccKey {
-    int dev, w;
-    bool staged;
-    size_t lds;
-};
-struct OccEntry {
-    OccKey key;
-    int cus, per_cu;
-};
-
-static bool occupancy(int w, bool staged, size_t lds, int &cus, int &per_cu) {
-    static std::mutex mu;
-    static OccEntry cache[64];
-    static int used = 0;
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) {
-        (void)hipGetLastError();  // clear it: the launch reports its own
-        return false;
-    }
-    {
-        std::lock_guard<std::mutex> lock(mu);
-        for (int i = 0; i < used; i++) {
-            const OccKey &k = cache[i].key;
-            if (k.dev == dev && k.w == w && k.staged == staged && k.lds == lds) {
-                cus = cache[i].cus;
-                per_cu = cache[i].per_cu;
-                return true;
-            }
-        }
-    }
-    const void *fn = nullptr;
-    if (staged) {
-        fn = w == 4 ? (const void *)dispatch_kernel<4, true>
-                    : w == 2 ? (const void *)dispatch_kernel<2, true> : (const void *)dispatch_kernel<1, true>;
-    } else {
-        fn = w == 4 ? (const void *)dispatch_kernel<4, false>
-                    : w == 2 ? (const void *)dispatch_kernel<2, false> : (const void *)dispatch_kernel<1, false>;
-    }
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, w * kWave, lds) != hipSuccess) {
-        (void)hipGetLastError();
-        return false;
-    }
-    std::lock_guard<std::mutex> lock(mu);
-    if (used < 64) cache[used++] = OccEntry{OccKey{dev, w, staged, lds}, cus, per_cu};
-    return true;
+static const void *dispatch_fn(int w, bool staged) {
+    if (staged)
+        return w == 4 ? (const void *)dispatch_kernel<4, true>
+                      : w == 2 ? (const void *)dispatch_kernel<2, true> : (const void *)dispatch_kernel<1, true>;
+    return w == 4 ? (const void *)dispatch_kernel<4, false>
+                  : w == 2 ? (const void *)dispatch_kernel<2, false> : (const void *)dispatch_kernel<1, false>;
 }
 
 static int resident_blocks(int w, bool staged, size_t lds) {
-    int cus = 0, per_cu = 0;
-    return occupancy(w, staged, lds, cus, per_cu) ? cus * per_cu : 0;
+    return ::ep::resident_blocks(dispatch_fn(w, staged), w * kWave, lds);
 }
 
 hipError_t launch_dispatch(const int32_t *ids, int64_t N, int32_t P, const ep_layout_t &L,
@@ -370,8 +324,11 @@ hipError_t launch_dispatch(const int32_t *ids, int64_t N, int32_t P, const ep_la
     // Staging turns the scatter of dispatch_src into runs, but its buffer
     // (2 bytes per pair of a sub-block) lowers occupancy; below 8 resident
     // waves per CU the direct scatter is faster.
-    int cus = 0, per_cu_unused = 0;
-    if (!occupancy(1, false, dispatch_lds_bytes(E, Phi, 1, 0), cus, per_cu_unused)) cus = 0;
+    int cus = 0, dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+        (void)hipGetLastError();
+        cus = 0;
+    }
     auto best_waves = [&](bool st, int &w_out) {
         const int w0 = pick_dispatch_waves(E, Phi, st ? sub : 0);
         int best = w0, waves = -1;

@@ -238,6 +238,11 @@ __device__ __forceinline__ void wave_lds_fence() {
     __builtin_amdgcn_wave_barrier();
 }
 
+// Workgroups of kernel `fn` (threads per workgroup, dynamic LDS bytes) that
+// the current device holds at once, 0 if unknown.  Cached per (device, fn,
+// threads, lds), so launches make no runtime queries after the first.
+int resident_blocks(const void *fn, int threads, size_t lds);
+
 // ---------------------------------------------------------------------------
 // launchers (defined in the .hip files; return hipError_t of the launch)
 // ---------------------------------------------------------------------------
