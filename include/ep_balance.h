@@ -203,6 +203,8 @@ int ep_reroute(const int32_t *topk_ids, int64_t pairs_per_plan, int32_t num_plan
  *                 padding, invalid IDs and pairs past the expert's quotas
  *   dispatch_src  device int32 [P][N] (written): pair index (within the plan)
  *                 at each position, -1 for positions no pair takes
+ * All output arrays 4-byte aligned.  LDS bounds the shape: 24 E + 12 Phi + 20
+ * bytes must fit 64 KiB (about E <= 1800 at Phi = E).
  */
 int ep_dispatch_layout(const int32_t *topk_ids, int64_t pairs_per_plan, int32_t num_plans,
                        const ep_layout_t *layout, const int32_t *phy_quota, const int32_t *log2phy,
@@ -236,7 +238,9 @@ int ep_slot_fill(const void *expert_weights, int64_t bytes_per_expert, const int
  *   native_grads device float [E][n] (in/out), 16-byte aligned
  *   slot_grads   device float [S][n], the gradient half of the slot buffer
  *   log2phy, logcnt  that layer's plan (ep_plan_quota)
- * n = elems_per_expert must be a positive multiple of 4.
+ * n = elems_per_expert must be a positive multiple of 4; requires rho <= 64 and
+ * E <= 65535.  Rows of experts whose instance list names a slot outside
+ * [0, Phi) are left unchanged.
  */
 int ep_replica_grad_reduce(float *native_grads, int64_t elems_per_expert, const float *slot_grads,
                            const int32_t *log2phy, const int32_t *logcnt, const ep_layout_t *layout,

@@ -4,6 +4,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <vector>
 
 #include "ep_internal.h"
@@ -85,14 +86,7 @@ int ep_layout_init(int32_t E, int32_t R, const int32_t *native_count, const int3
         rank_nat[r] = native_count[r];
         blk.assign(native_experts + in, native_experts + in + native_count[r]);
         in += native_count[r];
-        // natives of a rank in ascending logical ID (counting over the ID range
-        // would cost O(E) per rank; a small insertion sort is enough here)
-        for (size_t i = 1; i < blk.size(); i++)
-            for (size_t j = i; j > 0 && blk[j - 1] > blk[j]; j--) {
-                const int32_t x = blk[j];
-                blk[j] = blk[j - 1];
-                blk[j - 1] = x;
-            }
+        std::sort(blk.begin(), blk.end());  // natives of a rank in ascending logical ID
         for (int32_t e : blk) {
             if (e < 0 || e >= E || home_slot[e] != -1) return EP_ERR_INVALID_ARG;
             home_slot[e] = slot;
@@ -173,7 +167,9 @@ int ep_dispatch_layout(const int32_t *topk_ids, int64_t N, int32_t P, const ep_l
     if (!layout_ok(layout) || !pairs_ok(topk_ids, N, P) || !phy_quota || !log2phy || !logcnt ||
         !slot_offsets)
         return EP_ERR_INVALID_ARG;
-    if (N > 0 && (!dispatch_pos || !dispatch_src)) return EP_ERR_INVALID_ARG;
+    if (!aligned(slot_offsets, 4)) return EP_ERR_INVALID_ARG;
+    if (N > 0 && (!dispatch_pos || !dispatch_src || !aligned(dispatch_pos, 4) || !aligned(dispatch_src, 4)))
+        return EP_ERR_INVALID_ARG;
     const int E = layout->num_experts;
     if (dispatch_lds_bytes(E, layout->num_phys, 1, 0) > kMaxLds) return EP_ERR_INVALID_ARG;
     const size_t need = ws_bytes(N, P, E);
@@ -189,7 +185,7 @@ int ep_replica_grad_reduce(float *native_grads, int64_t elems_per_expert, const 
         return EP_ERR_INVALID_ARG;
     if (!native_grads || !aligned(native_grads, 16)) return EP_ERR_INVALID_ARG;
     if (layout->num_spare > 0 && (!slot_grads || !aligned(slot_grads, 16))) return EP_ERR_INVALID_ARG;
-    if (layout->num_experts > kMaxPlans) return EP_ERR_INVALID_ARG;
+    if (layout->num_experts > kMaxPlans || layout->max_replicas > 64) return EP_ERR_INVALID_ARG;
     return hip_rc(launch_grad_reduce(native_grads, elems_per_expert, slot_grads, log2phy, logcnt, *layout,
                                      as_stream(stream)));
 }

@@ -28,6 +28,7 @@ __global__ __launch_bounds__(kRedThreads) void grad_reduce_kernel(
     const int e = blockIdx.y;
     int c = logcnt[e];
     c = c > rho ? rho : c;
+    c = c > 64 ? 64 : c;  // the entry point admits rho <= 64 only
     if (c < 2) return;
     if (threadIdx.x < c) {
         const int s = log2phy[(int64_t)e * rho + threadIdx.x];

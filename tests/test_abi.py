@@ -81,3 +81,33 @@ def test_layout_init_rejects_bad_placement_on_host():
                           ctypes.cast(sc, ctypes.c_void_p), ctypes.cast(buf, ctypes.c_void_p), 64,
                           ctypes.byref(out))
     assert rc == ep.EP_ERR_INVALID_ARG
+
+
+def test_entry_points_reject_unsupported_shapes_on_host():
+    import moe_expert_load_layer_amd as ep
+    if not os.path.exists(ep.LIB_PATH):
+        pytest.skip("library not built")
+    L = ep.lib()
+    fake = ctypes.c_void_p(256)
+    # rho = min(R, 1 + S) = 100 > 64: the gradient fold keeps at most 64 rows
+    wide = ep._CLayout(100, 100, 200, 100, 100, 1, 1, 0, fake)
+    rc = L.ep_replica_grad_reduce(fake, 64, fake, fake, fake, ctypes.byref(wide), None)
+    assert rc == ep.EP_ERR_INVALID_ARG
+    rc = L.ep_plan_quota(fake, 1, ctypes.byref(wide), fake, fake, fake, fake, None, None, None)
+    assert rc == ep.EP_ERR_INVALID_ARG
+    # a negative domain size is not a layout
+    bad_dom = ep._CLayout(12, 8, 16, 4, 5, 2, 1, -1, fake)
+    rc = L.ep_plan_quota(fake, 1, ctypes.byref(bad_dom), fake, fake, fake, fake, None, None, None)
+    assert rc == ep.EP_ERR_INVALID_ARG
+    # the dispatch layout needs 4-byte aligned outputs
+    lay = ep._CLayout(12, 8, 16, 4, 5, 2, 1, 0, fake)
+    ws = L.ep_workspace_bytes(512, 1, 12)
+    rc = L.ep_dispatch_layout(fake, 512, 1, ctypes.byref(lay), fake, fake, fake, fake, ws, fake,
+                              ctypes.c_void_p(258), fake, None)
+    assert rc == ep.EP_ERR_INVALID_ARG
+    rc = L.ep_dispatch_layout(fake, 512, 1, ctypes.byref(lay), fake, fake, fake, fake, ws,
+                              ctypes.c_void_p(257), fake, fake, None)
+    assert rc == ep.EP_ERR_INVALID_ARG
+    # gradient rows must be a multiple of 4 floats
+    rc = L.ep_replica_grad_reduce(fake, 6, fake, fake, fake, ctypes.byref(lay), None)
+    assert rc == ep.EP_ERR_INVALID_ARG
