@@ -95,6 +95,38 @@ def _dev(t: torch.Tensor, dtype: torch.dtype, name: str) -> torch.Tensor:
     return t
 
 
+def _arg(t: Optional[torch.Tensor], dtype: torch.dtype, shape, name: str) -> torch.Tensor:
+    """A device tensor of exactly this dtype and shape: the kernels trust the sizes."""
+    if t is None:
+        raise EPBalanceError(f"{name} is required")
+    _dev(t, dtype, name)
+    if tuple(t.shape) != tuple(shape):
+        raise EPBalanceError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def _ids(t: torch.Tensor, name: str = "topk_ids"):
+    _dev(t, torch.int32, name)
+    if t.dim() != 2:
+        raise EPBalanceError(f"{name} must be [plans][pairs], got shape {tuple(t.shape)}")
+    return t.shape
+
+
+def _ws(ws: torch.Tensor, N: int, P: int, layout: "Layout") -> torch.Tensor:
+    if not (ws.is_cuda and ws.is_contiguous()):
+        raise EPBalanceError("ws must be a contiguous device tensor")
+    if ws.numel() * ws.element_size() < ep_workspace_bytes(N, P, layout.num_experts):
+        raise EPBalanceError("ws is smaller than ep_workspace_bytes(N, P, E)")
+    return ws
+
+
+def _plan_args(layout: "Layout", P: int, phy_quota, log2phy, logcnt):
+    E, Phi, rho = layout.num_experts, layout.num_phys, layout.max_replicas
+    _arg(phy_quota, torch.int32, (P, Phi), "phy_quota")
+    _arg(log2phy, torch.int32, (P, E, rho), "log2phy")
+    _arg(logcnt, torch.int32, (P, E), "logcnt")
+
+
 def _stream(stream: Optional[torch.cuda.Stream]):
     s = stream if stream is not None else torch.cuda.current_stream()
     return ctypes.c_void_p(s.cuda_stream)
@@ -160,13 +192,12 @@ def workspace(topk_ids: torch.Tensor, layout: Layout) -> torch.Tensor:
 def ep_load_histogram(topk_ids: torch.Tensor, layout: Layout, load=None, ws=None, status=None,
                       stream=None):
     """topk_ids int32 [P][N] -> (load int32 [P][E], ws, status uint32-as-int32 [P])."""
-    _dev(topk_ids, torch.int32, "topk_ids")
-    P, N = topk_ids.shape
+    P, N = _ids(topk_ids)
     dev = topk_ids.device
     load = torch.empty((P, layout.num_experts), dtype=torch.int32, device=dev) if load is None else load
-    ws = workspace(topk_ids, layout) if ws is None else ws
+    ws = workspace(topk_ids, layout) if ws is None else _ws(ws, N, P, layout)
     status = torch.empty(P, dtype=torch.int32, device=dev) if status is None else status
-    _dev(load, torch.int32, "load"); _dev(status, torch.int32, "status")
+    _arg(load, torch.int32, (P, layout.num_experts), "load"); _arg(status, torch.int32, (P,), "status")
     rc = lib().ep_load_histogram(_ptr(topk_ids), N, P, layout.ref(), _ptr(load), _ptr(ws),
                                  ws.numel() * ws.element_size(), _ptr(status), _stream(stream))
     _check(rc, "ep_load_histogram")
@@ -195,7 +226,13 @@ def ep_plan_quota(load: torch.Tensor, layout: Layout, out: Optional[PlanOut] = N
                   stream=None) -> PlanOut:
     _dev(load, torch.int32, "load")
     P = load.shape[0]
+    _arg(load, torch.int32, (P, layout.num_experts), "load")
     out = alloc_plan(P, layout, load.device) if out is None else out
+    _arg(out.phy2log, torch.int32, (P, layout.num_phys), "phy2log")
+    _plan_args(layout, P, out.phy_quota, out.log2phy, out.logcnt)
+    _arg(out.steps, torch.int32, (P,), "steps")
+    if status is not None:
+        _arg(status, torch.int32, (P,), "status")
     rc = lib().ep_plan_quota(_ptr(load), P, layout.ref(), _ptr(out.phy2log), _ptr(out.phy_quota),
                              _ptr(out.logcnt), _ptr(out.log2phy), _ptr(out.steps), _ptr(status),
                              _stream(stream))
@@ -205,11 +242,10 @@ def ep_plan_quota(load: torch.Tensor, layout: Layout, out: Optional[PlanOut] = N
 
 def ep_reroute(topk_ids: torch.Tensor, layout: Layout, phy_quota: torch.Tensor, log2phy: torch.Tensor,
                logcnt: torch.Tensor, ws: torch.Tensor, phys_ids=None, stream=None) -> torch.Tensor:
-    _dev(topk_ids, torch.int32, "topk_ids")
-    for t, n in ((phy_quota, "phy_quota"), (log2phy, "log2phy"), (logcnt, "logcnt")):
-        _dev(t, torch.int32, n)
-    P, N = topk_ids.shape
-    phys_ids = torch.empty_like(topk_ids) if phys_ids is None else phys_ids
+    P, N = _ids(topk_ids)
+    _plan_args(layout, P, phy_quota, log2phy, logcnt)
+    _ws(ws, N, P, layout)
+    phys_ids = torch.empty_like(topk_ids) if phys_ids is None else _arg(phys_ids, torch.int32, (P, N), "phys_ids")
     rc = lib().ep_reroute(_ptr(topk_ids), N, P, layout.ref(), _ptr(phy_quota), _ptr(log2phy),
                           _ptr(logcnt), _ptr(ws), ws.numel() * ws.element_size(), _ptr(phys_ids),
                           _stream(stream))
@@ -221,15 +257,16 @@ def ep_dispatch_layout(topk_ids: torch.Tensor, layout: Layout, phy_quota: torch.
                        log2phy: torch.Tensor, logcnt: torch.Tensor, ws: torch.Tensor, slot_offsets=None,
                        dispatch_pos=None, dispatch_src=None, stream=None):
     """-> (slot_offsets int32 [P][Phi+1], dispatch_pos int32 [P][N], dispatch_src int32 [P][N])."""
-    _dev(topk_ids, torch.int32, "topk_ids")
-    for t, n in ((phy_quota, "phy_quota"), (log2phy, "log2phy"), (logcnt, "logcnt")):
-        _dev(t, torch.int32, n)
-    P, N = topk_ids.shape
+    P, N = _ids(topk_ids)
+    _plan_args(layout, P, phy_quota, log2phy, logcnt)
+    _ws(ws, N, P, layout)
     dev = topk_ids.device
     if slot_offsets is None:
         slot_offsets = torch.empty((P, layout.num_phys + 1), dtype=torch.int32, device=dev)
+    _arg(slot_offsets, torch.int32, (P, layout.num_phys + 1), "slot_offsets")
     dispatch_pos = torch.empty_like(topk_ids) if dispatch_pos is None else dispatch_pos
     dispatch_src = torch.empty_like(topk_ids) if dispatch_src is None else dispatch_src
+    _arg(dispatch_pos, torch.int32, (P, N), "dispatch_pos"); _arg(dispatch_src, torch.int32, (P, N), "dispatch_src")
     rc = lib().ep_dispatch_layout(_ptr(topk_ids), N, P, layout.ref(), _ptr(phy_quota), _ptr(log2phy),
                                   _ptr(logcnt), _ptr(ws), ws.numel() * ws.element_size(),
                                   _ptr(slot_offsets), _ptr(dispatch_pos), _ptr(dispatch_src),
@@ -242,10 +279,13 @@ def ep_replica_grad_reduce(native_grads: torch.Tensor, slot_grads: torch.Tensor,
                            logcnt: torch.Tensor, layout: Layout, stream=None) -> torch.Tensor:
     """native_grads float32 [E][n] (in place), slot_grads float32 [S][n], one plan's log2phy/logcnt."""
     _dev(native_grads, torch.float32, "native_grads")
-    _dev(log2phy, torch.int32, "log2phy"); _dev(logcnt, torch.int32, "logcnt")
-    if layout.num_spare:
-        _dev(slot_grads, torch.float32, "slot_grads")
+    if native_grads.dim() != 2 or native_grads.shape[0] != layout.num_experts:
+        raise EPBalanceError(f"native_grads must be [E][n] with E = {layout.num_experts}")
     n = native_grads.shape[1]
+    _arg(log2phy, torch.int32, (layout.num_experts, layout.max_replicas), "log2phy")
+    _arg(logcnt, torch.int32, (layout.num_experts,), "logcnt")
+    if layout.num_spare:
+        _arg(slot_grads, torch.float32, (layout.num_spare, n), "slot_grads")
     rc = lib().ep_replica_grad_reduce(_ptr(native_grads), n, _ptr(slot_grads) if layout.num_spare else None,
                                       _ptr(log2phy), _ptr(logcnt), layout.ref(), _stream(stream))
     _check(rc, "ep_replica_grad_reduce")
@@ -258,8 +298,13 @@ def ep_slot_fill(expert_weights: torch.Tensor, phy2log: torch.Tensor, layout: La
     if not (expert_weights.is_cuda and slot_buf.is_cuda and expert_weights.is_contiguous()
             and slot_buf.is_contiguous()):
         raise EPBalanceError("weights and slot buffer must be contiguous device tensors")
-    _dev(phy2log, torch.int32, "phy2log")
-    bpe = expert_weights.numel() * expert_weights.element_size() // layout.num_experts
+    _arg(phy2log, torch.int32, (layout.num_phys,), "phy2log")
+    total = expert_weights.numel() * expert_weights.element_size()
+    if total % layout.num_experts != 0:
+        raise EPBalanceError("expert_weights must hold the same number of bytes for every expert")
+    bpe = total // layout.num_experts
+    if slot_buf.numel() * slot_buf.element_size() < layout.num_spare * bpe:
+        raise EPBalanceError("slot_buf is smaller than S * bytes_per_expert")
     rc = lib().ep_slot_fill(_ptr(expert_weights), bpe, _ptr(phy2log), layout.ref(), _ptr(slot_buf),
                             _stream(stream))
     _check(rc, "ep_slot_fill")
@@ -269,13 +314,18 @@ def ep_slot_fill(expert_weights: torch.Tensor, phy2log: torch.Tensor, layout: La
 def ep_balance_stats(load: torch.Tensor, phy_quota: torch.Tensor, layout: Layout, stats=None,
                      imbalance=None, rank_load=None, want_rank_load=True, stream=None):
     """-> (stats int64 [P][4], imbalance float64 [P][2], rank_load int32 [P][2][R] or None)."""
-    _dev(load, torch.int32, "load"); _dev(phy_quota, torch.int32, "phy_quota")
+    _dev(load, torch.int32, "load")
     P = load.shape[0]
+    _arg(load, torch.int32, (P, layout.num_experts), "load")
+    _arg(phy_quota, torch.int32, (P, layout.num_phys), "phy_quota")
     dev = load.device
     stats = torch.empty((P, 4), dtype=torch.int64, device=dev) if stats is None else stats
     imbalance = torch.empty((P, 2), dtype=torch.float64, device=dev) if imbalance is None else imbalance
     if rank_load is None and want_rank_load:
         rank_load = torch.empty((P, 2, layout.num_ranks), dtype=torch.int32, device=dev)
+    _arg(stats, torch.int64, (P, 4), "stats"); _arg(imbalance, torch.float64, (P, 2), "imbalance")
+    if rank_load is not None:
+        _arg(rank_load, torch.int32, (P, 2, layout.num_ranks), "rank_load")
     rc = lib().ep_balance_stats(_ptr(load), _ptr(phy_quota), P, layout.ref(), _ptr(stats),
                                 _ptr(imbalance), _ptr(rank_load), _stream(stream))
     _check(rc, "ep_balance_stats")

@@ -426,3 +426,41 @@ def test_plan_domain_random_layouts(dev, seed):
         out = ep.ep_plan_quota(torch.from_numpy(loads).to(dev), lay)
         torch.cuda.synchronize()
         _assert_plan_equal(out, refs)
+
+
+def test_binding_rejects_wrong_shapes(dev):
+    # the kernels trust the sizes, so the binding checks every tensor's shape
+    wl = W.get("tiny")
+    lay = ep.Layout.from_workload(wl, device=dev)
+    ids = W.make_ids(wl).to(dev)
+    P, N = ids.shape
+    E, Phi, rho = lay.num_experts, lay.num_phys, lay.max_replicas
+    load, ws, status = ep.ep_load_histogram(ids, lay)
+    with pytest.raises(ep.EPBalanceError):
+        ep.ep_load_histogram(ids, lay, load=torch.empty((P, E - 1), dtype=torch.int32, device=dev))
+    with pytest.raises(ep.EPBalanceError):
+        ep.ep_load_histogram(ids, lay, ws=ws[:4])
+    bad = ep.alloc_plan(P, lay, dev)
+    bad.log2phy = torch.empty((P, E, rho - 1), dtype=torch.int32, device=dev)
+    with pytest.raises(ep.EPBalanceError):
+        ep.ep_plan_quota(load, lay, out=bad)
+    plan = ep.ep_plan_quota(load, lay)
+    with pytest.raises(ep.EPBalanceError):
+        ep.ep_reroute(ids, lay, plan.phy_quota[:, :-1].contiguous(), plan.log2phy, plan.logcnt, ws)
+    with pytest.raises(ep.EPBalanceError):
+        ep.ep_reroute(ids, lay, plan.phy_quota, plan.log2phy, plan.logcnt, ws,
+                      phys_ids=torch.empty((P, N - 1), dtype=torch.int32, device=dev))
+    with pytest.raises(ep.EPBalanceError):
+        ep.ep_dispatch_layout(ids, lay, plan.phy_quota, plan.log2phy, plan.logcnt, ws,
+                              slot_offsets=torch.empty((P, Phi), dtype=torch.int32, device=dev))
+    with pytest.raises(ep.EPBalanceError):
+        ep.ep_balance_stats(load, plan.phy_quota, lay, stats=torch.empty((P, 4), dtype=torch.int32, device=dev))
+    with pytest.raises(ep.EPBalanceError):
+        ep.ep_slot_fill(torch.empty((E, 64), dtype=torch.bfloat16, device=dev), plan.phy2log[0][:-1].contiguous(),
+                        lay, torch.empty((lay.num_spare, 64), dtype=torch.bfloat16, device=dev))
+    with pytest.raises(ep.EPBalanceError):
+        ep.ep_replica_grad_reduce(torch.zeros((E, 8), device=dev), torch.zeros((lay.num_spare, 4), device=dev),
+                                  plan.log2phy[0].contiguous(), plan.logcnt[0].contiguous(), lay)
+    # the shapes the path itself uses still pass
+    ep.ep_reroute(ids, lay, plan.phy_quota, plan.log2phy, plan.logcnt, ws)
+    torch.cuda.synchronize()
