@@ -44,7 +44,7 @@ METRIC = "(token,k) pairs/s via hist+plan+reroute; plan µs/layer at EP64; HBM G
 # HBM bytes per slot-fill launch measured with rocprofv3 --pmc (FETCH_SIZE and
 # WRITE_SIZE), scaled by the same counters on a plain copy of known size; valid
 # only for the kernel source they were taken on.
-TRAFFIC = {"kernel_sha": "bd13ef8067a89f47", "fetch_kib": 1145030.5, "write_kib": 2290666.4, "fetch_scale": 2.0, "write_scale": 1.0, "bytes_per_launch": 4690610216}
+TRAFFIC = {"kernel_sha": "f464a1ef3130fe8f", "fetch_kib": 1145029.5, "write_kib": 2290666.3, "fetch_scale": 2.0, "write_scale": 1.0, "bytes_per_launch": 4690662837}
 
 
 def _src_sha(name: str) -> str:

@@ -2,8 +2,10 @@
 // designs: replicas live in slots reserved per rank, and one slot buffer is
 // reused by every layer).  For the o-th spare slot s with phy2log[s] = e >= 0,
 // expert e's weights are copied into row o of the slot buffer; empty slots are
-// not written.  A pure HBM-to-HBM stream: 16-byte non-temporal loads and
-// stores, each workgroup moving one 64 KiB chunk of one slot.
+// not written.  A pure HBM-to-HBM stream: 16-byte loads and stores, each
+// workgroup of 256 threads moving one 16 KiB chunk of one slot (short
+// workgroups measured fastest; non-temporal access and longer chunks were
+// slower).
 #include "ep_internal.h"
 
 namespace ep {
