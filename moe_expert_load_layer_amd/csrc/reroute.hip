@@ -200,6 +200,20 @@ __global__ __launch_bounds__(W *kWave) void reroute_kernel(
     int32_t *code = code_all + (size_t)wave * E;
     int32_t *srun = srun_all + (size_t)wave * E;
     int32_t *sidx = sidx_all + (size_t)wave * kWave;
+    // the first tiles of IDs load while the expert codes are set up (used by
+    // the 16-byte path below, which runs its first step under this same test)
+    i32x4 pf[EP_RR_UNROLL];
+    {
+        const int64_t b0 = sb * sub;
+        const int64_t b1 = (b0 + sub < N) ? b0 + sub : N;
+        const int32_t *s0 = ids + (int64_t)p * N + b0;
+        const int32_t *d0 = out + (int64_t)p * N + b0;
+        if (((((uintptr_t)s0 | (uintptr_t)d0) & 15) == 0) && (b1 - b0) / (4 * kWave) >= EP_RR_UNROLL) {
+#pragma unroll
+            for (int u = 0; u < EP_RR_UNROLL; u++)
+                pf[u] = __builtin_nontemporal_load(reinterpret_cast<const i32x4 *>(s0) + u * kWave + lane);
+        }
+    }
     // --- per-expert code for this sub-block
     const SubPrefix pre = sub_prefix(ws, p, sb, nsb, sps, nseg, E1);
     int nsplit = 0;
@@ -253,8 +267,13 @@ __global__ __launch_bounds__(W *kWave) void reroute_kernel(
         int64_t tt = 0;
         for (; tt + U <= ntile; tt += U) {
             i32x4 v[U];
+            if (tt == 0) {
 #pragma unroll
-            for (int u = 0; u < U; u++) v[u] = __builtin_nontemporal_load(s4 + (tt + u) * kWave + lane);
+                for (int u = 0; u < U; u++) v[u] = pf[u];
+            } else {
+#pragma unroll
+                for (int u = 0; u < U; u++) v[u] = __builtin_nontemporal_load(s4 + (tt + u) * kWave + lane);
+            }
 #pragma unroll
             for (int u = 0; u < U; u++) {
                 int32_t x[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
