@@ -60,10 +60,21 @@ __global__ __launch_bounds__(kHistWaves * kWave) void hist_kernel(
             const i32x4 *v4 = reinterpret_cast<const i32x4 *>(src + begin);
             constexpr int U = EP_HIST_UNROLL;
             int64_t k = lane;
+            // double-buffered: the next U vectors load while these U are counted
+            i32x4 nx[U];
+            if (k + (U - 1) * kWave < nvec) {
+#pragma unroll
+                for (int u = 0; u < U; u++) nx[u] = __builtin_nontemporal_load(v4 + k + u * kWave);
+            }
             for (; k + (U - 1) * kWave < nvec; k += U * kWave) {
                 i32x4 x[U];
 #pragma unroll
-                for (int u = 0; u < U; u++) x[u] = __builtin_nontemporal_load(v4 + k + u * kWave);
+                for (int u = 0; u < U; u++) x[u] = nx[u];
+                const int64_t kn = k + U * kWave;
+                if (kn + (U - 1) * kWave < nvec) {
+#pragma unroll
+                    for (int u = 0; u < U; u++) nx[u] = __builtin_nontemporal_load(v4 + kn + u * kWave);
+                }
 #pragma unroll
                 for (int u = 0; u < U; u++) {
                     count(x[u].x); count(x[u].y); count(x[u].z); count(x[u].w);

@@ -265,14 +265,17 @@ __global__ __launch_bounds__(W *kWave) void reroute_kernel(
         const i32x4 *s4 = reinterpret_cast<const i32x4 *>(src + begin);
         i32x4 *d4 = reinterpret_cast<i32x4 *>(dst + begin);
         int64_t tt = 0;
+        // double-buffered: the next U tiles load while these U are converted
+        i32x4 nv[U];
+#pragma unroll
+        for (int u = 0; u < U; u++) nv[u] = pf[u];
         for (; tt + U <= ntile; tt += U) {
             i32x4 v[U];
-            if (tt == 0) {
 #pragma unroll
-                for (int u = 0; u < U; u++) v[u] = pf[u];
-            } else {
+            for (int u = 0; u < U; u++) v[u] = nv[u];
+            if (tt + 2 * U <= ntile) {
 #pragma unroll
-                for (int u = 0; u < U; u++) v[u] = __builtin_nontemporal_load(s4 + (tt + u) * kWave + lane);
+                for (int u = 0; u < U; u++) nv[u] = __builtin_nontemporal_load(s4 + (tt + U + u) * kWave + lane);
             }
 #pragma unroll
             for (int u = 0; u < U; u++) {
