@@ -44,16 +44,34 @@ __global__ __launch_bounds__(kRedThreads) void grad_reduce_kernel(
     const int64_t c0 = (int64_t)blockIdx.x * kRedChunk;
     const int64_t c1 = (c0 + kRedChunk < vpe) ? c0 + kRedChunk : vpe;
     f32x4 *out = native + (int64_t)e * vpe;
-    for (int64_t i = c0 + threadIdx.x; i < c1; i += kRedThreads) {
-        f32x4 acc = rows[0][i];
-        for (int t = 1; t < c; t++) {
-            const f32x4 g = rows[t][i];
-            acc.x = acc.x + g.x;
-            acc.y = acc.y + g.y;
-            acc.z = acc.z + g.z;
-            acc.w = acc.w + g.w;
+    // all kRedIters vectors of a thread load together for each row (more
+    // loads in flight); each element still folds its rows in slot order
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    f32x4 acc[kRedIters];
+#pragma unroll
+    for (int k = 0; k < kRedIters; k++) {
+        const int64_t i = c0 + threadIdx.x + k * kRedThreads;
+        acc[k] = i < c1 ? rows[0][i] : zero;
+    }
+    for (int t = 1; t < c; t++) {
+        f32x4 g[kRedIters];
+#pragma unroll
+        for (int k = 0; k < kRedIters; k++) {
+            const int64_t i = c0 + threadIdx.x + k * kRedThreads;
+            g[k] = i < c1 ? rows[t][i] : zero;
         }
-        out[i] = acc;
+#pragma unroll
+        for (int k = 0; k < kRedIters; k++) {
+            acc[k].x = acc[k].x + g[k].x;
+            acc[k].y = acc[k].y + g[k].y;
+            acc[k].z = acc[k].z + g[k].z;
+            acc[k].w = acc[k].w + g[k].w;
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < kRedIters; k++) {
+        const int64_t i = c0 + threadIdx.x + k * kRedThreads;
+        if (i < c1) out[i] = acc[k];
     }
 }
 
