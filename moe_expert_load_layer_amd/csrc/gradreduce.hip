@@ -45,20 +45,21 @@ __global__ __launch_bounds__(kRedThreads) void grad_reduce_kernel(
     const int64_t c1 = (c0 + kRedChunk < vpe) ? c0 + kRedChunk : vpe;
     f32x4 *out = native + (int64_t)e * vpe;
     // all kRedIters vectors of a thread load together for each row (more
-    // loads in flight); each element still folds its rows in slot order
+    // loads in flight), non-temporal as every byte is touched once; each
+    // element still folds its rows in slot order
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     f32x4 acc[kRedIters];
 #pragma unroll
     for (int k = 0; k < kRedIters; k++) {
         const int64_t i = c0 + threadIdx.x + k * kRedThreads;
-        acc[k] = i < c1 ? rows[0][i] : zero;
+        acc[k] = i < c1 ? __builtin_nontemporal_load(rows[0] + i) : zero;
     }
     for (int t = 1; t < c; t++) {
         f32x4 g[kRedIters];
 #pragma unroll
         for (int k = 0; k < kRedIters; k++) {
             const int64_t i = c0 + threadIdx.x + k * kRedThreads;
-            g[k] = i < c1 ? rows[t][i] : zero;
+            g[k] = i < c1 ? __builtin_nontemporal_load(rows[t] + i) : zero;
         }
 #pragma unroll
         for (int k = 0; k < kRedIters; k++) {
@@ -71,7 +72,7 @@ __global__ __launch_bounds__(kRedThreads) void grad_reduce_kernel(
 #pragma unroll
     for (int k = 0; k < kRedIters; k++) {
         const int64_t i = c0 + threadIdx.x + k * kRedThreads;
-        if (i < c1) out[i] = acc[k];
+        if (i < c1) __builtin_nontemporal_store(acc[k], out + i);
     }
 }
 
