@@ -231,7 +231,7 @@ __global__ __launch_bounds__(W *kWave) void dispatch_kernel(
             if (cur.kf & kSplitFlag) pos = position_of(inst, rfirst[xi], rcnt[xi], cur.base + k);
             if (STAGED) stage[valid ? off + k : sub] = (uint16_t)(i - begin);
             else if (pos >= 0 && pos < N) src_out[pos] = (int32_t)i;
-            if (i < end) pos_out[i] = pos;
+            if (i < end) __builtin_nontemporal_store(pos, pos_out + i);
             wave_lds_fence();
         }
     }
