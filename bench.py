@@ -172,14 +172,16 @@ def main(argv=None) -> int:
             pp = run_chunks(cc)
             path_once(pp)
             xs = []
-            for _ in range(3):
+            for _ in range(5):
                 a = torch.cuda.Event(enable_timing=True); b = torch.cuda.Event(enable_timing=True)
                 a.record(stream); path_once(pp); b.record(stream)
                 xs.append((a, b))
             torch.cuda.synchronize()
             t_ms = statistics.median(_elapsed(xs))
             tuning["one stream" if cc == 1 else ",".join(map(str, cc))] = t_ms
-            if best_ms is None or t_ms < best_ms:
+            # overlap must win clearly: its gain is small where it exists and
+            # single timings vary by a few per cent
+            if best_ms is None or t_ms < best_ms * (0.98 if best == 1 else 1.0):
                 best, best_ms = cc, t_ms
             del pp
         chunks = best
