@@ -116,3 +116,36 @@ def test_fullsize_domain_plan(dev, name):
         for k in ("phy2log", "phy_quota", "logcnt", "log2phy"):
             assert np.array_equal(got[k][p], getattr(pl, k)), f"{k} plan {p}"
         assert got["steps"][p] == pl.steps
+
+
+def test_fullsize_overlapped_path_as_benched(dev):
+    # the launch configuration the benchmark times on this workload: the 94
+    # plans as chunks of 35 and 59 on three streams
+    wl = W.get("qwen3_235b")
+    P, N = wl.num_plans, wl.pairs_per_plan
+    print(f"[fullsize-overlap] {wl.name}: P={P} N={N} chunks 35+59", flush=True)
+    ids = W.make_ids(wl, device=dev)
+    lay = ep.Layout.from_workload(wl, device=dev)
+    load = torch.empty((P, wl.num_experts), dtype=torch.int32, device=dev)
+    status = torch.empty(P, dtype=torch.int32, device=dev)
+    plan = ep.alloc_plan(P, lay, dev)
+    phys = torch.empty_like(ids)
+    ep.PathPipeline(lay, P, N, chunks=[35, 59], device=dev).run(ids, load, status, plan, phys)
+    torch.cuda.synchronize()
+    ids_h = ids.cpu().numpy()
+    del ids
+    got = {k: v.cpu().numpy() for k, v in dict(load=load, status=status, phys=phys, quota=plan.phy_quota,
+                                                 l2p=plan.log2phy, steps=plan.steps).items()}
+    del phys
+    torch.cuda.empty_cache()
+    lay_o = oracle.Layout.from_workload(wl)
+    for p in range(P):
+        ld, bad = oracle.histogram(ids_h[p], wl.num_experts)
+        assert np.array_equal(got["load"][p], ld), f"load plan {p}"
+        pl = oracle.plan(ld, lay_o)
+        assert np.array_equal(got["quota"][p], pl.phy_quota), f"quota plan {p}"
+        assert np.array_equal(got["l2p"][p], pl.log2phy), f"log2phy plan {p}"
+        assert got["steps"][p] == pl.steps
+        assert got["status"][p] == (ep.EP_STATUS_STEP_CAP if pl.cap_hit else 0) | (ep.EP_STATUS_BAD_ID if bad else 0)
+        ph, _ = oracle.reroute(ids_h[p], wl.num_experts, pl.phy_quota, pl.log2phy, pl.logcnt)
+        assert np.array_equal(got["phys"][p], ph), f"reroute plan {p}"
