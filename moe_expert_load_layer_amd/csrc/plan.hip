@@ -529,7 +529,10 @@ static int pow2_at_least(int x) {
 
 int plan_lanes_cfg(const ep_layout_t &L) {
     if (L.num_ranks > kWave) return 0;
-    const int npr = pow2_at_least(L.max_rank_natives > 0 ? L.max_rank_natives : 1);
+    // natives per rank in registers: 1, 2, 4, 6 or 8 (6 saves a quarter of the
+    // work for layouts with 5 or 6 natives per rank)
+    const int mn = L.max_rank_natives > 0 ? L.max_rank_natives : 1;
+    const int npr = (mn > 4 && mn <= 6) ? 6 : pow2_at_least(mn);
     const int spr = pow2_at_least(L.max_rank_spares > 0 ? L.max_rank_spares : 1);
     if (npr > 8 || spr > 16 || lanes_lds_bytes(L) > 65536) return 0;
     return npr * 32 + spr;
@@ -554,6 +557,7 @@ hipError_t launch_plan(const int32_t *load, int32_t P, const ep_layout_t &L, int
         EP_LANES_ROW(1)
         EP_LANES_ROW(2)
         EP_LANES_ROW(4)
+        EP_LANES_ROW(6)
         EP_LANES_ROW(8)
         default:
             hipLaunchKernelGGL(plan_kernel_generic, g, b, plan_lds_bytes(L), s, load, a, phy2log,

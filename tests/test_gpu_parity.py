@@ -338,11 +338,13 @@ def test_deterministic_and_stream_independent(dev):
 
 
 # ------------------------------------------------ planner kernel selection
-# The library plans with one rank per lane when R <= 64 and every rank has at
-# most 16 spare slots (1, 2, 4, 8 or 16 spare registers per lane), and with the
-# generic LDS kernel otherwise; both must agree with the oracle.
+# The library plans with one rank per lane when R <= 64, every rank has at
+# most 8 natives (1, 2, 4, 6 or 8 native registers per lane) and at most 16
+# spare slots (1, 2, 4, 8 or 16 spare registers), and with the generic LDS
+# kernel otherwise; both must agree with the oracle.
 @pytest.mark.parametrize("R,E,max_sp", [(8, 20, 1), (16, 40, 2), (24, 50, 3), (32, 64, 7),
-                                        (12, 30, 13), (70, 140, 1), (90, 90, 0), (4, 12, 20)])
+                                        (12, 30, 13), (70, 140, 1), (90, 90, 0), (4, 12, 20),
+                                        (16, 80, 3), (10, 55, 2), (8, 60, 1), (6, 54, 2)])
 def test_plan_kernel_paths(dev, R, E, max_sp):
     rng = np.random.default_rng(R * 1000 + E)
     nc = np.full(R, E // R)
