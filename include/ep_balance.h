@@ -163,7 +163,11 @@ int ep_load_histogram(const int32_t *topk_ids, int64_t pairs_per_plan, int32_t n
  *   log2phy   device int32 [P][E][rho]: instance slots in ascending order, -1 padded
  *   steps     device int32 [P] or NULL: committed moves
  *   status    device uint32 [P] or NULL: EP_STATUS_STEP_CAP is OR-ed in
- * Requires rho <= 64 (at most 64 instances of one expert), 1 <= P <= 65535.
+ * Requires rho <= 64 (at most 64 instances of one expert), 1 <= P <= 65535,
+ * and either R <= 64 with at most 8 natives and 16 spare slots per rank, or
+ * tables that fit the generic kernel's 64 KiB of LDS (about 60 bytes per rank
+ * and per expert: R = E up to about 1050); other layouts return
+ * EP_ERR_INVALID_ARG.
  */
 int ep_plan_quota(const int32_t *load, int32_t num_plans, const ep_layout_t *layout,
                   int32_t *phy2log, int32_t *phy_quota, int32_t *logcnt, int32_t *log2phy,

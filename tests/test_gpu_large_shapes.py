@@ -1,0 +1,100 @@
+"""Layouts at the edges of what the kernels hold in LDS: many experts, many
+ranks (the generic planner), and the largest histogram.  Each runs the chain
+on the GPU and compares it with the CPU oracle bit for bit; shapes beyond a
+kernel's limit must be rejected, not run."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+ep = pytest.importorskip("moe_expert_load_layer_amd")
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def _layout(E, R, S, seed):
+    rng = np.random.default_rng(seed)
+    nc = np.full(R, E // R)
+    nc[: E % R] += 1
+    ne = rng.permutation(E)
+    sc = np.zeros(R, np.int64)
+    sc[rng.permutation(R)[:S]] = 1
+    return [int(x) for x in nc], [int(x) for x in ne], [int(x) for x in sc]
+
+
+def _ids(E, P, N, seed):
+    rng = np.random.default_rng(seed)
+    out = np.empty((P, N), np.int32)
+    for p in range(P):
+        cdf = np.cumsum(rng.dirichlet(np.full(E, 0.2)))
+        out[p] = np.minimum(np.searchsorted(cdf, rng.random(N), side="right"), E - 1)
+    out[:, ::211] = -1
+    return out
+
+
+@pytest.mark.parametrize("E,R,S", [(1500, 100, 63), (1024, 1024, 63), (1200, 64, 63)])
+def test_large_layouts_full_chain(dev, E, R, S):
+    # (1500, 100) and (1024, 1024): the generic planner near its LDS limit;
+    # (1200, 64): 19 natives per rank, also the generic planner
+    nc, ne, sc = _layout(E, R, S, E + R)
+    P, N = 2, 300_007
+    ids_h = _ids(E, P, N, E * 7 + R)
+    print(f"[large] E={E} R={R} S={S} P={P} N={N}", flush=True)
+    lay = ep.Layout.create(E, nc, ne, sc, device=dev)
+    ids = torch.from_numpy(ids_h).to(dev)
+    out = ep.run_path(ids, lay)
+    pl = out["plan"]
+    off, pos, src = ep.ep_dispatch_layout(ids, lay, pl.phy_quota, pl.log2phy, pl.logcnt, out["ws"])
+    torch.cuda.synchronize()
+    lay_o = oracle.Layout.of(E, R, nc, ne, sc)
+    for p in range(P):
+        ld, _ = oracle.histogram(ids_h[p], E)
+        assert np.array_equal(out["load"][p].cpu().numpy(), ld)
+        r = oracle.plan(ld, lay_o)
+        assert np.array_equal(pl.phy_quota[p].cpu().numpy(), r.phy_quota)
+        assert np.array_equal(pl.log2phy[p].cpu().numpy(), r.log2phy)
+        assert int(pl.steps[p]) == r.steps
+        ph, _ = oracle.reroute(ids_h[p], E, r.phy_quota, r.log2phy, r.logcnt)
+        assert np.array_equal(out["phys"][p].cpu().numpy(), ph)
+        ro, rp, rs, _ = oracle.dispatch(ids_h[p], E, r.phy_quota, r.log2phy, r.logcnt)
+        assert np.array_equal(off[p].cpu().numpy().astype(np.int64), ro)
+        assert np.array_equal(pos[p].cpu().numpy(), rp)
+        assert np.array_equal(src[p].cpu().numpy(), rs)
+
+
+def test_largest_histogram_and_reroute(dev):
+    # E = 2047 fills the histogram's LDS exactly (8 waves x 2048 counters); 32
+    # natives per rank are beyond both planner kernels, so the planner must
+    # refuse and the reroute runs on the oracle's plan
+    E, R, S = 2047, 64, 64
+    nc, ne, sc = _layout(E, R, S, 9)
+    P, N = 2, 400_003
+    ids_h = _ids(E, P, N, 11)
+    lay = ep.Layout.create(E, nc, ne, sc, device=dev)
+    ids = torch.from_numpy(ids_h).to(dev)
+    load, ws, status = ep.ep_load_histogram(ids, lay)
+    with pytest.raises(ep.EPBalanceError):
+        ep.ep_plan_quota(load, lay)
+    lay_o = oracle.Layout.of(E, R, nc, ne, sc)
+    plans = [oracle.plan(oracle.histogram(ids_h[p], E)[0], lay_o) for p in range(P)]
+    st = lambda k: torch.from_numpy(np.stack([getattr(r, k) for r in plans])).to(dev)
+    phys = ep.ep_reroute(ids, lay, st("phy_quota"), st("log2phy"), st("logcnt"), ws)
+    torch.cuda.synchronize()
+    for p in range(P):
+        ld, _ = oracle.histogram(ids_h[p], E)
+        assert np.array_equal(load[p].cpu().numpy(), ld)
+        ph, _ = oracle.reroute(ids_h[p], E, plans[p].phy_quota, plans[p].log2phy, plans[p].logcnt)
+        assert np.array_equal(phys[p].cpu().numpy(), ph)
+    # one expert more is beyond the histogram's LDS
+    nc2, ne2, sc2 = _layout(E + 1, R, S, 10)
+    lay2 = ep.Layout.create(E + 1, nc2, ne2, sc2, device=dev)
+    with pytest.raises(ep.EPBalanceError):
+        ep.ep_load_histogram(ids, lay2)
