@@ -98,3 +98,34 @@ def test_largest_histogram_and_reroute(dev):
     lay2 = ep.Layout.create(E + 1, nc2, ne2, sc2, device=dev)
     with pytest.raises(ep.EPBalanceError):
         ep.ep_load_histogram(ids, lay2)
+
+
+def test_most_plans_per_call(dev):
+    # P = 65535 plans (the grid's y extent) of 13 pairs each on the Tiny layout
+    E, R = 12, 8
+    nc, ne, sc = [2, 2, 2, 2, 1, 1, 1, 1], list(range(12)), [0, 0, 0, 0, 1, 1, 1, 1]
+    P, N = 65535, 13
+    rng = np.random.default_rng(65535)
+    ids_h = rng.integers(-1, E, size=(P, N), dtype=np.int32)
+    ids_h[:, 0] = rng.integers(0, 3, size=P)           # a hot expert per plan
+    print(f"[plans] P={P} N={N}", flush=True)
+    lay = ep.Layout.create(E, nc, ne, sc, device=dev)
+    ids = torch.from_numpy(ids_h).to(dev)
+    out = ep.run_path(ids, lay)
+    torch.cuda.synchronize()
+    load = out["load"].cpu().numpy(); q = out["plan"].phy_quota.cpu().numpy()
+    phys = out["phys"].cpu().numpy(); st = out["stats"].cpu().numpy()
+    lay_o = oracle.Layout.of(E, R, nc, ne, sc)
+    for p in list(range(0, P, 97)) + [P - 1]:
+        ld, _ = oracle.histogram(ids_h[p], E)
+        assert np.array_equal(load[p], ld), p
+        r = oracle.plan(ld, lay_o)
+        assert np.array_equal(q[p], r.phy_quota), p
+        ph, _ = oracle.reroute(ids_h[p], E, r.phy_quota, r.log2phy, r.logcnt)
+        assert np.array_equal(phys[p], ph), p
+        assert np.array_equal(st[p], oracle.stats(ld, r.phy_quota, lay_o).as_row()), p
+    # every plan's loads are exact (a property that holds at any size)
+    ref = np.stack([np.bincount(row[row >= 0], minlength=E) for row in ids_h])
+    assert np.array_equal(load, ref)
+    with pytest.raises(ep.EPBalanceError):
+        ep.ep_load_histogram(torch.zeros((P + 1, N), dtype=torch.int32, device=dev), lay)
