@@ -129,3 +129,32 @@ def test_most_plans_per_call(dev):
     assert np.array_equal(load, ref)
     with pytest.raises(ep.EPBalanceError):
         ep.ep_load_histogram(torch.zeros((P + 1, N), dtype=torch.int32, device=dev), lay)
+
+
+def test_most_spare_slots_in_slot_fill(dev):
+    # 65535 spare slots (the slot fill's grid y extent), every one given a
+    # random expert or left empty; one slot more is refused
+    E, R = 64, 64
+    S = 65535
+    nc, ne = [1] * R, list(range(E))
+    sc = [S // R + (1 if r < S % R else 0) for r in range(R)]
+    lay = ep.Layout.create(E, nc, ne, sc, device=dev)
+    lay_o = oracle.Layout.of(E, R, nc, ne, sc)
+    first, home, rank, spare = lay_o.slots()
+    rng = np.random.default_rng(4)
+    phy2log = home.astype(np.int32).copy()
+    phy2log[spare] = rng.integers(-1, E, size=S)
+    w = rng.integers(0, 1 << 16, size=(E, 48), dtype=np.uint16)
+    ref = np.full((S, 48), 0x7FC1, np.uint16)
+    oracle.slot_fill(w, phy2log, lay_o, ref)
+    buf = torch.from_numpy(np.full((S, 48), 0x7FC1, np.uint16).view(np.int16)).to(dev)
+    ep.ep_slot_fill(torch.from_numpy(w.view(np.int16)).to(dev), torch.from_numpy(phy2log).to(dev), lay, buf)
+    torch.cuda.synchronize()
+    assert np.array_equal(buf.cpu().numpy().view(np.uint16), ref)
+    sc2 = list(sc)
+    sc2[0] += 1
+    lay2 = ep.Layout.create(E, nc, ne, sc2, device=dev)
+    with pytest.raises(ep.EPBalanceError):
+        ep.ep_slot_fill(torch.from_numpy(w.view(np.int16)).to(dev),
+                        torch.zeros(lay2.num_phys, dtype=torch.int32, device=dev), lay2,
+                        torch.zeros((S + 1, 48), dtype=torch.int16, device=dev))
