@@ -4,9 +4,11 @@
 // and update the load distribution; the load lives in fixed spare slots).
 //
 // One wave (one workgroup of 64 lanes) per plan; plans of many layers and
-// microbatches run side by side in one launch.  All state sits in LDS:
-//   rank loads, free spare counts, slot owners and quotas, per-expert
-//   instance counts.
+// microbatches run side by side in one launch.  Two kernels: the generic one
+// below keeps all state in LDS (rank loads, free spare counts, slot owners and
+// quotas, per-expert instance counts) and takes any R; the rank-per-lane one
+// further down keeps each rank's state in its lane's registers (R <= 64) and
+// is the one the workloads here use.  Both make the same moves.
 // Each step:
 //   1. hottest rank h   = wave max of the packed key (load << 32 | ~rank);
 //   2. candidates       = loaded instances on h, visited in descending
@@ -269,8 +271,12 @@ __global__ __launch_bounds__(kWave) void plan_kernel_generic(const int32_t *__re
 // readlane; the instances of an expert are found lane-locally (its native
 // lane, or a lane holding it in a spare slot); the water-fill runs over the
 // lanes that host the expert and a commit only touches their registers.  LDS
-// holds the static (native rank, native index) of every expert and, at the
-// end, the per-expert masks of replica ranks used to order log2phy.
+// holds the static (native rank, native index) of every expert, a per-expert
+// flag that says whether a re-level could change the expert's quotas (set
+// when a commit moves the load of a rank that hosts it, cleared when the
+// expert itself is levelled; candidates whose flag is clear are not tried in
+// the re-level pass), and, at the end, the per-expert masks of replica ranks
+// used to order log2phy.
 // ---------------------------------------------------------------------------
 template <int N>
 __device__ __forceinline__ int32_t pick(const int32_t (&v)[N], int i) {
