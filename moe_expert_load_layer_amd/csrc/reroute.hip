@@ -12,7 +12,9 @@
 // (sub-block, expert) cells are rare; only their pairs are ranked one by one:
 // per split expert, a wave prefix sum over lanes of the counts in flat order.
 // Everything else is one LDS read per pair, and the IDs stream in and the
-// physical IDs stream out as 16-byte accesses.
+// physical IDs stream out as 16-byte non-temporal accesses: the first tiles
+// load while the code table is built, later ones one step ahead of their use.
+// Short waves (one sub-block each) keep HBM busier than persistent ones.
 #include "ep_internal.h"
 
 namespace ep {
