@@ -350,6 +350,24 @@ def main(argv=None) -> int:
             "status_nonzero": int((status != 0).sum().item()),
         },
     }
+    if wl.microbatches > 1:
+        # History-based placement for comparison: each plan uses the replicas
+        # planned for the same layer of the previous microbatch, and an
+        # expert's pairs are split evenly over its instances.  Real-time
+        # planning on the exact loads is what `imbalance_after` reports.
+        nc = np.asarray(wl.native_count); sc = np.asarray(wl.spare_count)
+        slot_rank = np.repeat(np.arange(wl.num_ranks), nc + sc)
+        p2l = plan.phy2log.cpu().numpy(); ld = load.cpu().numpy().astype(np.float64)
+        stale = []
+        for p in range(wl.layers, P):
+            prev = p2l[p - wl.layers]
+            used_slots = prev >= 0
+            cnt = np.bincount(prev[used_slots], minlength=E)
+            share = ld[p][prev[used_slots]] / cnt[prev[used_slots]]
+            rank_load = np.bincount(slot_rank[used_slots], weights=share, minlength=wl.num_ranks)
+            stale.append(rank_load.max() * wl.num_ranks / max(ld[p].sum(), 1.0))
+        out["balance"]["previous_microbatch_placement_imbalance_mean"] = float(np.mean(stale))
+        out["balance"]["previous_microbatch_placement_imbalance_max"] = float(np.max(stale))
 
     if args.cpu_budget > 0:
         ids_host = ids.cpu().numpy()
