@@ -251,8 +251,12 @@ def main(argv=None) -> int:
         ep.ep_plan_quota(load, lay, out=plan, status=status)
         ep.ep_reroute(ids, lay, plan.phy_quota, plan.log2phy, plan.logcnt, ws, phys_ids=phys)
     ph_serial = lat(serial, 10) * 1e-3
-    hist_gbps = 4.0 * P * N / (ph_hist * 1e-3) / 1e9
-    rr_gbps = 8.0 * P * N / (ph_rr * 1e-3) / 1e9
+    # algorithmic bytes per pair: with E <= 256 the histogram also writes a
+    # one-byte copy of each ID (4 in, 1 out), which the reroute reads instead
+    # of the int32 ID (1 in, 4 out); otherwise 4 in, and 4 in + 4 out
+    hist_bpp, rr_bpp = (5.0, 5.0) if E <= 256 else (4.0, 8.0)
+    hist_gbps = hist_bpp * P * N / (ph_hist * 1e-3) / 1e9
+    rr_gbps = rr_bpp * P * N / (ph_rr * 1e-3) / 1e9
 
     ids1 = ids[:1]
     load1 = load[:1].clone()
@@ -333,6 +337,7 @@ def main(argv=None) -> int:
         "path_chunks": [b - a for a, b in pipe.bounds] if pipe is not None else [P],
         "path_chunk_tuning_ms": tuning,
         "kernels": {
+            "hist_bytes_per_pair": hist_bpp, "reroute_bytes_per_pair": rr_bpp,
             "hist_GBps": hist_gbps, "hist_frac": hist_gbps / HBM_PEAK_GBPS,
             "reroute_GBps": rr_gbps, "reroute_frac": rr_gbps / HBM_PEAK_GBPS,
             "plan_us_per_layer_batched": ph_plan * 1e3 / P,

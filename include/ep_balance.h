@@ -114,9 +114,12 @@ int ep_layout_init(int32_t num_experts, int32_t num_ranks, const int32_t *native
  * per-expert pair counts from the histogram to the reroute (and the dispatch
  * layout): for every sub-block of consecutive pairs, how many pairs of each
  * expert come before it in the plan, stored as a count within a segment of
- * sub-blocks plus a per-segment base.  Pass the same buffer, untouched in
- * between, with the same N and P.  Grows as P * (sub-blocks + segments + 1) *
- * (E + 1) * 4, about 1/8 to 1/4 byte per pair.
+ * sub-blocks plus a per-segment base.  With E <= 256 it also holds a one-byte
+ * copy of every ID and a flag per sub-block (padding or IDs >= E present),
+ * which the reroute reads in place of the int32 IDs of unflagged sub-blocks.
+ * Pass the same buffer, untouched in between, with the same N and P.  Grows
+ * as P * (sub-blocks + segments + 1) * (E + 1) * 4, about 1/8 to 1/4 byte per
+ * pair, plus about 1 byte per pair with E <= 256.
  */
 size_t ep_workspace_bytes(int64_t pairs_per_plan, int32_t num_plans, int32_t num_experts);
 
@@ -180,7 +183,11 @@ int ep_plan_quota(const int32_t *load, int32_t num_plans, const ep_layout_t *lay
  * looked up from the top-k logical ID).  The j-th pair (0-based, flat order)
  * of expert e goes to the instance i (ascending slot order) with
  * Q_i <= j < Q_i + quota_i, Q_i the sum of the quotas of the instances before i.
- *   topk_ids  device int32 [P][N], the same IDs the histogram saw
+ *   topk_ids  device int32 [P][N], the same IDs the histogram saw (with
+ *             E <= 256 most pairs are read from the workspace's byte copy;
+ *             pairs are read here only in sub-blocks that hold padding or bad
+ *             IDs, where phys_ids is not 16-byte aligned, and after a
+ *             sub-block's last whole 256-pair tile)
  *   phy_quota, log2phy, logcnt: a plan as ep_plan_quota writes it (each
  *             instance a distinct slot in [0, Phi), logcnt in [0, rho])
  *   ws        the workspace filled by ep_load_histogram for these IDs

@@ -131,7 +131,8 @@ int ep_load_histogram(const int32_t *topk_ids, int64_t N, int32_t P, const ep_la
     if ((size_t)kSegSubs * (E + 1) * 4 > kMaxLds) return EP_ERR_INVALID_ARG;
     const size_t need = ws_bytes(N, P, E);
     if (ws_size < need || (need > 0 && (!ws || !aligned(ws, 16)))) return EP_ERR_INVALID_ARG;
-    return hip_rc(launch_histogram(topk_ids, N, P, E, sub_geom(N, P, E), static_cast<int32_t *>(ws), load, status, as_stream(stream)));
+    return hip_rc(launch_histogram(topk_ids, N, P, E, sub_geom(N, P, E), static_cast<int32_t *>(ws),
+                                   compact_of(ws, N, P, E), load, status, as_stream(stream)));
 }
 
 int ep_plan_quota(const int32_t *load, int32_t P, const ep_layout_t *layout, int32_t *phy2log,
@@ -156,8 +157,9 @@ int ep_reroute(const int32_t *topk_ids, int64_t N, int32_t P, const ep_layout_t 
     if (reroute_lds_bytes(E, layout->num_phys, 1) > kMaxLds) return EP_ERR_INVALID_ARG;
     const size_t need = ws_bytes(N, P, E);
     if (ws_size < need || (need > 0 && (!ws || !aligned(ws, 16)))) return EP_ERR_INVALID_ARG;
-    return hip_rc(launch_reroute(topk_ids, N, P, *layout, sub_geom(N, P, E), static_cast<const int32_t *>(ws), phy_quota, log2phy, logcnt,
-                                 phys_ids, as_stream(stream)));
+    return hip_rc(launch_reroute(topk_ids, N, P, *layout, sub_geom(N, P, E), static_cast<const int32_t *>(ws),
+                                 compact_of(const_cast<void *>(ws), N, P, E), phy_quota, log2phy,
+                                 logcnt, phys_ids, as_stream(stream)));
 }
 
 int ep_dispatch_layout(const int32_t *topk_ids, int64_t N, int32_t P, const ep_layout_t *layout,

@@ -113,9 +113,72 @@ inline SubGeom sub_geom(int64_t N, int32_t P, int32_t E) {
     return g;
 }
 
-inline size_t ws_bytes(int64_t N, int32_t P, int32_t E) {
+// ---------------------------------------------------------------------------
+// Compact IDs (E <= 256).  Besides counting, the histogram stores every pair's
+// ID as one byte and, per sub-block, a flag that is set when the sub-block
+// holds padding or an ID >= E.  The reroute of an unflagged sub-block reads
+// the bytes instead of the int32 IDs, so the IDs cross HBM as 4 + 1 (written)
+// + 1 bytes per pair instead of 4 + 4.  Workspace parts, each 256-byte aligned:
+//   count rows  int32 [P][nsb + nseg + 1][E + 1]  (above)
+//   flags       int32 [P][nsb]                     (compact only)
+//   bytes       uint8 [P][nb], nb = N rounded up to 16 (compact only)
+// ---------------------------------------------------------------------------
+constexpr int32_t kCompactMaxE = 256;
+inline bool compact_ids(int32_t E) { return E <= kCompactMaxE; }
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+inline int64_t compact_stride(int64_t N) { return (N + 15) & ~(int64_t)15; }
+
+struct WsParts {
+    size_t flags, bytes, total;  // byte offsets of the compact parts (0: none), total size
+};
+
+inline WsParts ws_parts(int64_t N, int32_t P, int32_t E) {
     const SubGeom g = sub_geom(N, P, E);
-    return (size_t)P * (size_t)(g.nsb + g.nseg + 1) * (size_t)(E + 1) * sizeof(int32_t);
+    const size_t rows = (size_t)P * (size_t)(g.nsb + g.nseg + 1) * (size_t)(E + 1) * sizeof(int32_t);
+    WsParts w{0, 0, rows};
+    if (compact_ids(E) && g.nsb > 0) {
+        w.flags = align256(rows);
+        w.bytes = w.flags + align256((size_t)P * (size_t)g.nsb * sizeof(int32_t));
+        w.total = w.bytes + (size_t)P * (size_t)compact_stride(N);
+    }
+    return w;
+}
+
+inline size_t ws_bytes(int64_t N, int32_t P, int32_t E) { return ws_parts(N, P, E).total; }
+
+// Byte order of the copy within a sub-block.  Whole groups of 1024 pairs (4
+// tiles of 256: lane l holds pairs 4l..4l+3 of a tile) are stored lane-major,
+// lane l's 16 bytes holding its 4 IDs of each of the 4 tiles, so that one
+// 16-byte access per lane moves a group; the pairs after the last whole group
+// are stored in order.
+constexpr int kGroupTiles = 4;
+constexpr int64_t kTilePairs = 4 * kWave;
+constexpr int64_t kGroupPairs = kGroupTiles * kTilePairs;
+
+// byte offset of pair j of a sub-block with `ngroup` whole groups
+__device__ __forceinline__ int64_t compact_pos(int64_t j, int64_t ngroup) {
+    if (j >= ngroup * kGroupPairs) return j;
+    const int64_t g = j / kGroupPairs;
+    const int r = (int)(j - g * kGroupPairs);
+    const int tile = r / (int)kTilePairs, l = (r % (int)kTilePairs) / 4, k = r % 4;
+    return g * kGroupPairs + l * 16 + tile * 4 + k;
+}
+
+// Device pointers of the compact parts of a workspace (null when E > 256).
+struct Compact {
+    int32_t *flags;  // [P][nsb]
+    uint8_t *bytes;  // [P][stride]
+    int64_t stride;
+};
+
+inline Compact compact_of(void *ws, int64_t N, int32_t P, int32_t E) {
+    const WsParts w = ws_parts(N, P, E);
+    Compact c{nullptr, nullptr, compact_stride(N)};
+    if (w.flags) {
+        c.flags = reinterpret_cast<int32_t *>(static_cast<unsigned char *>(ws) + w.flags);
+        c.bytes = static_cast<uint8_t *>(ws) + w.bytes;
+    }
+    return c;
 }
 
 // Per-expert pair counts of plan p before sub-block sb (start) and before
@@ -247,7 +310,8 @@ int resident_blocks(const void *fn, int threads, size_t lds);
 // launchers (defined in the .hip files; return hipError_t of the launch)
 // ---------------------------------------------------------------------------
 hipError_t launch_histogram(const int32_t *ids, int64_t N, int32_t P, int32_t E, const SubGeom &g,
-                            int32_t *ws, int32_t *load, uint32_t *status, hipStream_t s);
+                            int32_t *ws, const Compact &cp, int32_t *load, uint32_t *status,
+                            hipStream_t s);
 // cfg > 0 selects the rank-per-lane planner (32 * natives + spares registers
 // per lane, see plan_lanes_cfg); cfg == 0 selects the generic planner
 hipError_t launch_plan(const int32_t *load, int32_t P, const ep_layout_t &L, int32_t *phy2log,
@@ -256,9 +320,9 @@ hipError_t launch_plan(const int32_t *load, int32_t P, const ep_layout_t &L, int
 size_t plan_lds_bytes(const ep_layout_t &L);
 int plan_lanes_cfg(const ep_layout_t &L);
 hipError_t launch_reroute(const int32_t *ids, int64_t N, int32_t P, const ep_layout_t &L,
-                          const SubGeom &g, const int32_t *ws, const int32_t *phy_quota,
-                          const int32_t *log2phy, const int32_t *logcnt, int32_t *out,
-                          hipStream_t s);
+                          const SubGeom &g, const int32_t *ws, const Compact &cp,
+                          const int32_t *phy_quota, const int32_t *log2phy, const int32_t *logcnt,
+                          int32_t *out, hipStream_t s);
 size_t reroute_lds_bytes(int E, int Phi, int waves);
 hipError_t launch_dispatch(const int32_t *ids, int64_t N, int32_t P, const ep_layout_t &L,
                            const SubGeom &g, const int32_t *ws, const int32_t *phy_quota,

@@ -8,7 +8,14 @@
 //                LDS integer atomics, the IDs streaming in as 16-byte loads.
 //                After a barrier each wave stores its sub-block's in-segment
 //                prefix (the sum of the lower waves' histograms) and the last
-//                wave also the segment's totals.
+//                wave also the segment's totals.  With E <= 256 each wave also
+//                stores its pairs' IDs as bytes (16 per lane per 1024-pair
+//                group) and a flag that says whether the sub-block holds
+//                padding or an ID >= E, for the reroute to read instead of
+//                the int32 IDs.  The bytes go out as ordinary (cached)
+//                stores: the histogram alone is slower than with streaming
+//                stores, but a reroute that follows soon finds part of them
+//                in the caches, and the whole path is faster.
 //   scan_kernel  per (plan, 64 experts): inclusive scan of the segment totals
 //                in place, which leaves base[j] = pairs of segments < j and
 //                base[nseg] = the plan's total; writes load[p][e] and the
@@ -19,14 +26,18 @@
 namespace ep {
 namespace {
 
-#ifndef EP_HIST_UNROLL
-#define EP_HIST_UNROLL 4
-#endif
 constexpr int kHistWaves = kSegSubs;
+
+// the low bytes of four IDs, first ID in the lowest byte
+__device__ __forceinline__ uint32_t pack_bytes(i32x4 x) {
+    return ((uint32_t)x.x & 0xffu) | (((uint32_t)x.y & 0xffu) << 8) | (((uint32_t)x.z & 0xffu) << 16) |
+           ((uint32_t)x.w << 24);
+}
 
 __global__ __launch_bounds__(kHistWaves * kWave) void hist_kernel(
     const int32_t *__restrict__ ids, int64_t N, int32_t E, int64_t sub, int64_t nsb,
-    int64_t nseg, int32_t *__restrict__ ws) {
+    int64_t nseg, int32_t *__restrict__ ws, int32_t *__restrict__ flags, uint8_t *__restrict__ ids8,
+    int64_t stride8) {
     extern __shared__ int32_t sh_hist[];
     const int wave = threadIdx.x / kWave;
     const int lane = threadIdx.x % kWave;
@@ -42,52 +53,71 @@ __global__ __launch_bounds__(kHistWaves * kWave) void hist_kernel(
     const int32_t *src = ids + (int64_t)p * N;
     const uint32_t uE = (uint32_t)E;
     int nbad = 0;
+    bool odd = false;  // padding or an ID >= E seen
     auto count = [&](int32_t v) {
         if ((uint32_t)v < uE) {
             atomicAdd(&h[v], 1);
-        } else if (v >= E) {
-            nbad++;
+        } else {
+            odd = true;
+            if (v >= E) nbad++;
         }
     };
+    uint8_t *row8 = ids8 ? ids8 + (int64_t)p * stride8 : nullptr;
 
     if (sb < nsb) {  // waves past the plan's last sub-block keep an empty histogram
         const int64_t begin = sb * sub;
         const int64_t end = (begin + sub < N) ? begin + sub : N;
         int64_t i = begin;
+        const int64_t ngroup = (end - begin) / kGroupPairs;
         // 16-byte path: the plan row and sub-block start are 16-byte aligned
         if (((uintptr_t)(src + begin) & 15) == 0) {
             const int64_t nvec = (end - begin) / 4;
             const i32x4 *v4 = reinterpret_cast<const i32x4 *>(src + begin);
-            constexpr int U = EP_HIST_UNROLL;
-            int64_t k = lane;
-            // double-buffered: the next U vectors load while these U are counted
+            constexpr int U = kGroupTiles;
+            // whole groups, double-buffered: the next group loads while this
+            // one is counted; lane l's IDs of the group go out as 16 bytes
             i32x4 nx[U];
-            if (k + (U - 1) * kWave < nvec) {
+            if (ngroup > 0) {
 #pragma unroll
-                for (int u = 0; u < U; u++) nx[u] = __builtin_nontemporal_load(v4 + k + u * kWave);
+                for (int u = 0; u < U; u++) nx[u] = __builtin_nontemporal_load(v4 + lane + u * kWave);
             }
-            for (; k + (U - 1) * kWave < nvec; k += U * kWave) {
+            for (int64_t gi = 0; gi < ngroup; gi++) {
                 i32x4 x[U];
 #pragma unroll
                 for (int u = 0; u < U; u++) x[u] = nx[u];
-                const int64_t kn = k + U * kWave;
-                if (kn + (U - 1) * kWave < nvec) {
+                if (gi + 1 < ngroup) {
 #pragma unroll
-                    for (int u = 0; u < U; u++) nx[u] = __builtin_nontemporal_load(v4 + kn + u * kWave);
+                    for (int u = 0; u < U; u++)
+                        nx[u] = __builtin_nontemporal_load(v4 + (gi + 1) * U * kWave + lane + u * kWave);
                 }
 #pragma unroll
                 for (int u = 0; u < U; u++) {
                     count(x[u].x); count(x[u].y); count(x[u].z); count(x[u].w);
                 }
+                if (row8) {
+                    u32x4 b;
+                    b.x = pack_bytes(x[0]); b.y = pack_bytes(x[1]); b.z = pack_bytes(x[2]); b.w = pack_bytes(x[3]);
+                    reinterpret_cast<u32x4 *>(row8 + begin)[gi * kWave + lane] = b;
+                }
             }
-            for (; k < nvec; k += kWave) {
+            // the rest of the whole vectors; their bytes in pair order
+            for (int64_t k = ngroup * U * kWave + lane; k < nvec; k += kWave) {
                 const i32x4 x = __builtin_nontemporal_load(v4 + k);
                 count(x.x); count(x.y); count(x.z); count(x.w);
+                if (row8) __builtin_nontemporal_store(pack_bytes(x), reinterpret_cast<uint32_t *>(row8 + begin) + k);
             }
             i = begin + nvec * 4;
         }
-        for (int64_t j = i + lane; j < end; j += kWave) count(src[j]);
+        for (int64_t j = i + lane; j < end; j += kWave) {
+            const int32_t v = src[j];
+            count(v);
+            if (row8) row8[begin + compact_pos(j - begin, ngroup)] = (uint8_t)v;
+        }
         if (nbad) atomicAdd(&h[E], nbad);
+        if (flags) {
+            const bool any = __ballot(odd) != 0;
+            if (lane == 0) flags[(int64_t)p * nsb + sb] = any ? 1 : 0;
+        }
     }
     __syncthreads();
 
@@ -174,13 +204,14 @@ __global__ __launch_bounds__(kScanWaves * kWave) void scan_kernel(
 }  // namespace
 
 hipError_t launch_histogram(const int32_t *ids, int64_t N, int32_t P, int32_t E, const SubGeom &g,
-                            int32_t *ws, int32_t *load, uint32_t *status, hipStream_t s) {
+                            int32_t *ws, const Compact &cp, int32_t *load, uint32_t *status,
+                            hipStream_t s) {
     if (g.sps != kHistWaves) return hipErrorInvalidValue;
     if (g.nseg > 0) {
         dim3 grid((unsigned)g.nseg, (unsigned)P);
         const size_t lds = (size_t)kHistWaves * (E + 1) * sizeof(int32_t);
         hipLaunchKernelGGL(hist_kernel, grid, dim3(kHistWaves * kWave), lds, s, ids, N, E, g.sub,
-                           g.nsb, g.nseg, ws);
+                           g.nsb, g.nseg, ws, cp.flags, cp.bytes, cp.stride);
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }

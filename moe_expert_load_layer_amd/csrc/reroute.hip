@@ -12,8 +12,11 @@
 // (sub-block, expert) cells are rare; only their pairs are ranked one by one:
 // per split expert, a wave prefix sum over lanes of the counts in flat order.
 // Everything else is one LDS read per pair, and the IDs stream in and the
-// physical IDs stream out as 16-byte non-temporal accesses: the first tiles
-// load while the code table is built, later ones one step ahead of their use.
+// physical IDs stream out as non-temporal accesses: the first tiles load while
+// the code table is built, later ones one step ahead of their use.  With
+// E <= 256 the IDs come from the histogram's one-byte copy (16 bytes per lane
+// per 1024-pair group) unless the sub-block holds padding or bad IDs, which
+// read the int32 IDs (16 bytes per lane per 256-pair tile).
 // Short waves (one sub-block each) keep HBM busier than persistent ones.
 #include "ep_internal.h"
 
@@ -24,7 +27,7 @@ namespace {
 #define EP_RR_UNROLL 4
 #endif
 #ifndef EP_RR_MAX_WAVES
-#define EP_RR_MAX_WAVES 4
+#define EP_RR_MAX_WAVES 8
 #endif
 
 constexpr int32_t kSplit = (int32_t)0x80000000;
@@ -148,6 +151,7 @@ __global__ __launch_bounds__(W *kWave) void reroute_kernel(
     const int32_t *__restrict__ ids, int64_t N, int32_t E, int32_t Phi, int32_t rho, int64_t sub,
     int64_t nsb, int64_t sps, int64_t nseg, const int32_t *__restrict__ ws, const int32_t *__restrict__ phy_quota,
     const int32_t *__restrict__ log2phy, const int32_t *__restrict__ logcnt,
+    const int32_t *__restrict__ flags, const uint8_t *__restrict__ ids8, int64_t stride8,
     int32_t *__restrict__ out) {
     extern __shared__ __align__(16) unsigned char sh_raw[];
     int2 *inst = reinterpret_cast<int2 *>(sh_raw);                        // [Phi] (end, phys)
@@ -202,19 +206,29 @@ __global__ __launch_bounds__(W *kWave) void reroute_kernel(
     int32_t *code = code_all + (size_t)wave * E;
     int32_t *srun = srun_all + (size_t)wave * E;
     int32_t *sidx = sidx_all + (size_t)wave * kWave;
-    // the first tiles of IDs load while the expert codes are set up (used by
-    // the 16-byte path below, which runs its first step under this same test)
-    i32x4 pf[EP_RR_UNROLL];
-    {
-        const int64_t b0 = sb * sub;
-        const int64_t b1 = (b0 + sub < N) ? b0 + sub : N;
-        const int32_t *s0 = ids + (int64_t)p * N + b0;
-        const int32_t *d0 = out + (int64_t)p * N + b0;
-        if (((((uintptr_t)s0 | (uintptr_t)d0) & 15) == 0) && (b1 - b0) / (4 * kWave) >= EP_RR_UNROLL) {
+    const int64_t begin = sb * sub;
+    const int64_t end = (begin + sub < N) ? begin + sub : N;
+    const int32_t *src = ids + (int64_t)p * N;
+    int32_t *dst = out + (int64_t)p * N;
+    const int64_t ntile = (end - begin) / (4 * kWave);  // whole 256-pair tiles
+    const bool dst16 = (((uintptr_t)(dst + begin)) & 15) == 0;
+    const bool src16 = (((uintptr_t)(src + begin)) & 15) == 0;
+    const uint32_t *s8 = ids8 ? reinterpret_cast<const uint32_t *>(ids8 + (int64_t)p * stride8 + begin) : nullptr;
+    const int32_t odd = ids8 ? flags[(int64_t)p * nsb + sb] : 1;
+    // the first IDs load while the expert codes are set up: bytes when there
+    // is a compact copy (a flagged sub-block discards them), else int32
+    constexpr int U = EP_RR_UNROLL;
+    static_assert(U == kGroupTiles, "one group of the byte copy per step");
+    const int64_t ngroup = ntile / kGroupTiles;  // whole 1024-pair groups of the byte copy
+    i32x4 pf[U];
+    u32x4 pf8;
+    const bool pf_bytes = s8 && dst16 && ngroup > 0;
+    const bool pf_words = !s8 && dst16 && src16 && ntile >= U;
+    if (pf_bytes) pf8 = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(s8) + lane);
+    if (pf_words) {
 #pragma unroll
-            for (int u = 0; u < EP_RR_UNROLL; u++)
-                pf[u] = __builtin_nontemporal_load(reinterpret_cast<const i32x4 *>(s0) + u * kWave + lane);
-        }
+        for (int u = 0; u < U; u++)
+            pf[u] = __builtin_nontemporal_load(reinterpret_cast<const i32x4 *>(src + begin) + u * kWave + lane);
     }
     // --- per-expert code for this sub-block
     const SubPrefix pre = sub_prefix(ws, p, sb, nsb, sps, nseg, E1);
@@ -253,24 +267,61 @@ __global__ __launch_bounds__(W *kWave) void reroute_kernel(
         seek(sr, inst);
     }
 
-    const int64_t begin = sb * sub;
-    const int64_t end = (begin + sub < N) ? begin + sub : N;
-    const int32_t *src = ids + (int64_t)p * N;
-    int32_t *dst = out + (int64_t)p * N;
     const uint32_t uE = (uint32_t)E;
     int64_t g = begin;
-
-    // 16-byte path over whole 256-pair tiles
-    if ((((uintptr_t)(src + begin) | (uintptr_t)(dst + begin)) & 15) == 0) {
-        constexpr int U = EP_RR_UNROLL;
-        const int64_t ntile = (end - begin) / (4 * kWave);
-        const i32x4 *s4 = reinterpret_cast<const i32x4 *>(src + begin);
-        i32x4 *d4 = reinterpret_cast<i32x4 *>(dst + begin);
-        int64_t tt = 0;
-        // double-buffered: the next U tiles load while these U are converted
-        i32x4 nv[U];
+    i32x4 *d4 = reinterpret_cast<i32x4 *>(dst + begin);
+    // physical IDs of the 4 pairs of lane `lane` in tile tt
+    auto emit = [&](int32_t (&x)[4], int64_t tt) {
+        int32_t c[4];
+        bool sp = false;
 #pragma unroll
-        for (int u = 0; u < U; u++) nv[u] = pf[u];
+        for (int k = 0; k < 4; k++) {
+            c[k] = (uint32_t)x[k] < uE ? code[x[k]] : -1;
+            sp |= is_split(c[k]);
+        }
+        if (__ballot(sp)) resolve_split<4>(x, c, sr, rfirst, rcnt, inst, srun);
+        i32x4 o;
+        o.x = c[0]; o.y = c[1]; o.z = c[2]; o.w = c[3];
+        __builtin_nontemporal_store(o, d4 + tt * kWave + lane);
+    };
+
+    if (s8 && dst16 && odd == 0) {
+        // one-byte IDs: a whole group is one 16-byte load per lane (its 4 IDs
+        // of each of the 4 tiles); double-buffered, the next group loads while
+        // this one is converted.  Whole tiles after the last group hold their
+        // bytes in pair order.
+        const u32x4 *g8 = reinterpret_cast<const u32x4 *>(s8);
+        u32x4 nw = pf8;
+        for (int64_t gi = 0; gi < ngroup; gi++) {
+            const u32x4 wv = nw;
+            if (gi + 1 < ngroup) nw = __builtin_nontemporal_load(g8 + (gi + 1) * kWave + lane);
+            const uint32_t w[U] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+            for (int u = 0; u < U; u++) {
+                int32_t x[4] = {(int32_t)(w[u] & 0xffu), (int32_t)((w[u] >> 8) & 0xffu),
+                                (int32_t)((w[u] >> 16) & 0xffu), (int32_t)(w[u] >> 24)};
+                emit(x, gi * U + u);
+            }
+        }
+        for (int64_t tt = ngroup * U; tt < ntile; tt++) {
+            const uint32_t w = __builtin_nontemporal_load(s8 + tt * kWave + lane);
+            int32_t x[4] = {(int32_t)(w & 0xffu), (int32_t)((w >> 8) & 0xffu), (int32_t)((w >> 16) & 0xffu),
+                            (int32_t)(w >> 24)};
+            emit(x, tt);
+        }
+        g = begin + ntile * 4 * kWave;
+    } else if (dst16 && src16) {
+        // int32 IDs, 16 bytes per lane per tile, double-buffered likewise
+        const i32x4 *s4 = reinterpret_cast<const i32x4 *>(src + begin);
+        int64_t tt = 0;
+        i32x4 nv[U];
+        if (pf_words) {
+#pragma unroll
+            for (int u = 0; u < U; u++) nv[u] = pf[u];
+        } else if (ntile >= U) {
+#pragma unroll
+            for (int u = 0; u < U; u++) nv[u] = __builtin_nontemporal_load(s4 + u * kWave + lane);
+        }
         for (; tt + U <= ntile; tt += U) {
             i32x4 v[U];
 #pragma unroll
@@ -282,33 +333,13 @@ __global__ __launch_bounds__(W *kWave) void reroute_kernel(
 #pragma unroll
             for (int u = 0; u < U; u++) {
                 int32_t x[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-                int32_t c[4];
-                bool sp = false;
-#pragma unroll
-                for (int k = 0; k < 4; k++) {
-                    c[k] = (uint32_t)x[k] < uE ? code[x[k]] : -1;
-                    sp |= is_split(c[k]);
-                }
-                if (__ballot(sp)) resolve_split<4>(x, c, sr, rfirst, rcnt, inst, srun);
-                i32x4 o;
-                o.x = c[0]; o.y = c[1]; o.z = c[2]; o.w = c[3];
-                __builtin_nontemporal_store(o, d4 + (tt + u) * kWave + lane);
+                emit(x, tt + u);
             }
         }
         for (; tt < ntile; tt++) {
             const i32x4 v = __builtin_nontemporal_load(s4 + tt * kWave + lane);
             int32_t x[4] = {v.x, v.y, v.z, v.w};
-            int32_t c[4];
-            bool sp = false;
-#pragma unroll
-            for (int k = 0; k < 4; k++) {
-                c[k] = (uint32_t)x[k] < uE ? code[x[k]] : -1;
-                sp |= is_split(c[k]);
-            }
-            if (__ballot(sp)) resolve_split<4>(x, c, sr, rfirst, rcnt, inst, srun);
-            i32x4 o;
-            o.x = c[0]; o.y = c[1]; o.z = c[2]; o.w = c[3];
-            __builtin_nontemporal_store(o, d4 + tt * kWave + lane);
+            emit(x, tt);
         }
         g = begin + ntile * 4 * kWave;
     }
@@ -335,9 +366,9 @@ size_t reroute_lds_bytes(int E, int Phi, int waves) {
 }
 
 hipError_t launch_reroute(const int32_t *ids, int64_t N, int32_t P, const ep_layout_t &L,
-                          const SubGeom &g, const int32_t *ws, const int32_t *phy_quota,
-                          const int32_t *log2phy, const int32_t *logcnt, int32_t *out,
-                          hipStream_t s) {
+                          const SubGeom &g, const int32_t *ws, const Compact &cp,
+                          const int32_t *phy_quota, const int32_t *log2phy, const int32_t *logcnt,
+                          int32_t *out, hipStream_t s) {
     const int64_t sub = g.sub, nsb = g.nsb, sps = g.sps, nseg = g.nseg;
     if (nsb == 0) return hipSuccess;
     const int E = L.num_experts, Phi = L.num_phys, rho = L.max_replicas;
@@ -348,19 +379,19 @@ hipError_t launch_reroute(const int32_t *ids, int64_t N, int32_t P, const ep_lay
     switch (w) {
         case 8:
             hipLaunchKernelGGL(reroute_kernel<8>, grid, dim3(8 * kWave), lds, s, ids, N, E, Phi,
-                               rho, sub, nsb, sps, nseg, ws, phy_quota, log2phy, logcnt, out);
+                               rho, sub, nsb, sps, nseg, ws, phy_quota, log2phy, logcnt, cp.flags, cp.bytes, cp.stride, out);
             break;
         case 4:
             hipLaunchKernelGGL(reroute_kernel<4>, grid, dim3(4 * kWave), lds, s, ids, N, E, Phi,
-                               rho, sub, nsb, sps, nseg, ws, phy_quota, log2phy, logcnt, out);
+                               rho, sub, nsb, sps, nseg, ws, phy_quota, log2phy, logcnt, cp.flags, cp.bytes, cp.stride, out);
             break;
         case 2:
             hipLaunchKernelGGL(reroute_kernel<2>, grid, dim3(2 * kWave), lds, s, ids, N, E, Phi,
-                               rho, sub, nsb, sps, nseg, ws, phy_quota, log2phy, logcnt, out);
+                               rho, sub, nsb, sps, nseg, ws, phy_quota, log2phy, logcnt, cp.flags, cp.bytes, cp.stride, out);
             break;
         default:
             hipLaunchKernelGGL(reroute_kernel<1>, grid, dim3(kWave), lds, s, ids, N, E, Phi, rho,
-                               sub, nsb, sps, nseg, ws, phy_quota, log2phy, logcnt, out);
+                               sub, nsb, sps, nseg, ws, phy_quota, log2phy, logcnt, cp.flags, cp.bytes, cp.stride, out);
             break;
     }
     return hipGetLastError();

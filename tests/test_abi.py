@@ -44,11 +44,16 @@ def test_host_side_checks_without_gpu():
     assert L.ep_layout_table_ints(12, 8, 4) == 2 * 8 + 1 + 3 * 16 + 12 + 4
     assert L.ep_workspace_bytes(-1, 1, 4) == 0
     assert L.ep_workspace_bytes(0, 3, 4) == 3 * 1 * 5 * 4      # only the per-plan totals row
-    # workspace grows with the number of sub-blocks
-    a = L.ep_workspace_bytes(1 << 20, 1, 128)
-    b = L.ep_workspace_bytes(1 << 21, 1, 128)
+    # workspace grows with the number of sub-blocks: count rows of E + 1 ints
+    a = L.ep_workspace_bytes(1 << 20, 1, 300)
+    b = L.ep_workspace_bytes(1 << 21, 1, 300)
     assert 0 < a < b
-    assert a % (129 * 4) == 0
+    assert a % (301 * 4) == 0
+    # E <= 256 adds the one-byte copy of the IDs and a flag per sub-block
+    rows = L.ep_workspace_bytes(1 << 20, 1, 257)
+    c = L.ep_workspace_bytes(1 << 20, 1, 256)
+    assert (1 << 20) + rows <= c < (1 << 20) + rows + 4096    # rows, flags, bytes (256-byte aligned)
+    assert L.ep_workspace_bytes(1000, 2, 8) >= 2 * 1008
     # null pointers are rejected before any device work
     lay = ep._CLayout(12, 8, 16, 4, 5, 2, 1, 0, None)
     rc = L.ep_load_histogram(None, 512, 1, ctypes.byref(lay), None, None, 0, None, None)
