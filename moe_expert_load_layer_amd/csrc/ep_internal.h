@@ -272,27 +272,31 @@ __device__ __forceinline__ int64_t readlane_i64(int64_t v, int lane) {
     return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
-// Row-level (16-lane) DPP reductions finished with four readlanes: no LDS
-// traffic.  dpp controls: quad_perm [1,0,3,2] = 0xB1, [2,3,0,1] = 0x4E,
-// row_half_mirror = 0x141, row_mirror = 0x140.
+// Wave-wide max / min without LDS: four DPP steps inside each row of 16 lanes
+// (quad_perm [1,0,3,2] = 0xB1, [2,3,0,1] = 0x4E, row_half_mirror = 0x141,
+// row_mirror = 0x140, fused into the max / min), then gfx950's lane swaps
+// across rows (permlane16) and halves (permlane32).  All 64 lanes must be
+// active: bound_ctrl reads 0 from a disabled lane.
 __device__ __forceinline__ int wave_max_i32(int v) {
-    v = max(v, __builtin_amdgcn_update_dpp(v, v, 0xB1, 0xF, 0xF, false));
-    v = max(v, __builtin_amdgcn_update_dpp(v, v, 0x4E, 0xF, 0xF, false));
-    v = max(v, __builtin_amdgcn_update_dpp(v, v, 0x141, 0xF, 0xF, false));
-    v = max(v, __builtin_amdgcn_update_dpp(v, v, 0x140, 0xF, 0xF, false));
-    const int a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
-    const int c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
-    return max(max(a, b), max(c, d));
+    v = max(v, __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, true));
+    v = max(v, __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, true));
+    v = max(v, __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, true));
+    v = max(v, __builtin_amdgcn_mov_dpp(v, 0x140, 0xF, 0xF, true));
+    const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    v = max((int)a[0], (int)a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return __builtin_amdgcn_readfirstlane(max((int)b[0], (int)b[1]));
 }
 
 __device__ __forceinline__ int wave_min_i32(int v) {
-    v = min(v, __builtin_amdgcn_update_dpp(v, v, 0xB1, 0xF, 0xF, false));
-    v = min(v, __builtin_amdgcn_update_dpp(v, v, 0x4E, 0xF, 0xF, false));
-    v = min(v, __builtin_amdgcn_update_dpp(v, v, 0x141, 0xF, 0xF, false));
-    v = min(v, __builtin_amdgcn_update_dpp(v, v, 0x140, 0xF, 0xF, false));
-    const int a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
-    const int c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
-    return min(min(a, b), min(c, d));
+    v = min(v, __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, true));
+    v = min(v, __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, true));
+    v = min(v, __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, true));
+    v = min(v, __builtin_amdgcn_mov_dpp(v, 0x140, 0xF, 0xF, true));
+    const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    v = min((int)a[0], (int)a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return __builtin_amdgcn_readfirstlane(min((int)b[0], (int)b[1]));
 }
 
 // orders LDS accesses of the lanes of one wave (no workgroup barrier)
