@@ -359,6 +359,13 @@ __global__ __launch_bounds__(kWave) void plan_kernel_lanes(const int32_t *__rest
             if (lane == NPR + j) { ce = e; cq = q; }
         }
         const bool valid = ce >= 0 && cq > 0;
+        // LDS reads of the candidates (dirty flag; native rank and index of a
+        // replica's expert) go out before the ordering below, which hides them
+        int cdirty = 0, cpk = 0;
+        if (valid) {
+            cdirty = edirty[ce];
+            if (cnr < 0) cpk = nri[ce];
+        }
         const uint64_t key = valid ? (((uint64_t)(uint32_t)cq << 32) | inv((uint32_t)ce)) : 0;
         // order of the candidates: count the larger keys
         const uint64_t vm = __ballot(valid);
@@ -370,7 +377,7 @@ __global__ __launch_bounds__(kWave) void plan_kernel_lanes(const int32_t *__rest
         }
         const int nc = __popcll(vm);
         // candidates worth a re-level: replicated and set in edirty
-        const uint64_t relevel = __ballot(valid && cic >= 2 && edirty[valid ? ce : 0] != 0);
+        const uint64_t relevel = __ballot(valid && cic >= 2 && cdirty != 0);
 
         bool committed = false;
         for (int pass = relevel ? 0 : 1; pass < 2 && !committed; pass++) {
@@ -384,9 +391,9 @@ __global__ __launch_bounds__(kWave) void plan_kernel_lanes(const int32_t *__rest
                     idx = __builtin_amdgcn_readlane(cidx, cl);
                     T = __builtin_amdgcn_readlane(cld, cl);
                 } else {
-                    const int packed = nri[e];
-                    nr = __builtin_amdgcn_readfirstlane(packed >> 8);
-                    idx = __builtin_amdgcn_readfirstlane(packed & 0xff);
+                    const int packed = __builtin_amdgcn_readlane(cpk, cl);
+                    nr = packed >> 8;
+                    idx = packed & 0xff;
                     T = __builtin_amdgcn_readlane(pick(nat_ld, idx), nr);
                 }
                 const bool replicate = pass == 1;
