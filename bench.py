@@ -240,17 +240,32 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
         return statistics.median(_elapsed(xs)) * 1e3   # us
 
+    # throughput of back-to-back calls: events around `per` calls, median of
+    # `reps` such runs, per call (the launch gaps of a lone call do not count)
+    def run_ms(fn, reps, per=4):
+        xs = []
+        for _ in range(2):
+            fn()
+        for _ in range(reps):
+            a = ev()
+            for _ in range(per):
+                fn()
+            b = ev()
+            xs.append((a, b))
+        torch.cuda.synchronize()
+        return statistics.median(_elapsed(xs)) / per
+
     # the path's phases one at a time, all plans per launch
-    ph_hist = lat(lambda: ep.ep_load_histogram(ids, lay, load=load, ws=ws, status=status), 10) * 1e-3
-    ph_plan = lat(lambda: ep.ep_plan_quota(load, lay, out=plan, status=status), 10) * 1e-3
-    ph_rr = lat(lambda: ep.ep_reroute(ids, lay, plan.phy_quota, plan.log2phy, plan.logcnt, ws,
-                                      phys_ids=phys), 10) * 1e-3
+    ph_hist = run_ms(lambda: ep.ep_load_histogram(ids, lay, load=load, ws=ws, status=status), 5)
+    ph_plan = run_ms(lambda: ep.ep_plan_quota(load, lay, out=plan, status=status), 5)
+    ph_rr = run_ms(lambda: ep.ep_reroute(ids, lay, plan.phy_quota, plan.log2phy, plan.logcnt, ws,
+                                         phys_ids=phys), 5)
     # the same path as one stream of three launches, for comparison
     def serial():
         ep.ep_load_histogram(ids, lay, load=load, ws=ws, status=status)
         ep.ep_plan_quota(load, lay, out=plan, status=status)
         ep.ep_reroute(ids, lay, plan.phy_quota, plan.log2phy, plan.logcnt, ws, phys_ids=phys)
-    ph_serial = lat(serial, 10) * 1e-3
+    ph_serial = run_ms(serial, 5)
     # algorithmic bytes per pair: with E <= 256 the histogram also writes a
     # one-byte copy of each ID (4 in, 1 out), which the reroute reads instead
     # of the int32 ID (1 in, 4 out); otherwise 4 in, and 4 in + 4 out

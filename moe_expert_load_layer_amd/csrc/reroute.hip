@@ -152,8 +152,11 @@ __device__ __forceinline__ void resolve_split(const int32_t (&x)[K], int32_t (&c
     }
 }
 
-template <int W>
-__global__ __launch_bounds__(W *kWave) void reroute_kernel(
+// At most 72 VGPRs (7 waves per SIMD; the compiler moves a few values of the
+// rare split path to scratch): 5 % faster than the 78 it picks unbounded, at
+// 8 waves (64 VGPRs) the spills cost more than the waves gain.
+template <int W, bool BYTES>
+__global__ __launch_bounds__(W *kWave, 7) void reroute_kernel(
     const int32_t *__restrict__ ids, int64_t N, int32_t E, int32_t Phi, int32_t rho, int64_t sub,
     int64_t nsb, int64_t sps, int64_t nseg, const int32_t *__restrict__ ws, const int32_t *__restrict__ phy_quota,
     const int32_t *__restrict__ log2phy, const int32_t *__restrict__ logcnt,
@@ -228,8 +231,8 @@ __global__ __launch_bounds__(W *kWave) void reroute_kernel(
     const int64_t ngroup = ntile / kGroupTiles;  // whole 1024-pair groups of the byte copy
     i32x4 pf[U];
     u32x4 pf8[kPfGroups];  // the next groups of the byte copy, in order
-    const bool pf_bytes = s8 && dst16 && ngroup > 0;
-    const bool pf_words = !s8 && dst16 && src16 && ntile >= U;
+    const bool pf_bytes = BYTES && s8 && dst16 && ngroup > 0;
+    const bool pf_words = !BYTES && dst16 && src16 && ntile >= U;
     if (pf_bytes) {
 #pragma unroll
         for (int j = 0; j < kPfGroups; j++)
@@ -295,7 +298,7 @@ __global__ __launch_bounds__(W *kWave) void reroute_kernel(
         __builtin_nontemporal_store(o, d4 + tt * kWave + lane);
     };
 
-    if (s8 && dst16 && odd == 0) {
+    if (BYTES && s8 && dst16 && odd == 0) {
         // one-byte IDs: a whole group is one 16-byte load per lane (its 4 IDs
         // of each of the 4 tiles), kPfGroups groups ahead of their use.
         // Whole tiles after the last group hold their bytes in pair order.
@@ -387,24 +390,17 @@ hipError_t launch_reroute(const int32_t *ids, int64_t N, int32_t P, const ep_lay
     if (w == 0) return hipErrorInvalidValue;
     const size_t lds = reroute_lds_bytes(E, Phi, w);
     dim3 grid((unsigned)((nsb + w - 1) / w), (unsigned)P);
-    switch (w) {
-        case 8:
-            hipLaunchKernelGGL(reroute_kernel<8>, grid, dim3(8 * kWave), lds, s, ids, N, E, Phi,
-                               rho, sub, nsb, sps, nseg, ws, phy_quota, log2phy, logcnt, cp.flags, cp.bytes, cp.stride, out);
-            break;
-        case 4:
-            hipLaunchKernelGGL(reroute_kernel<4>, grid, dim3(4 * kWave), lds, s, ids, N, E, Phi,
-                               rho, sub, nsb, sps, nseg, ws, phy_quota, log2phy, logcnt, cp.flags, cp.bytes, cp.stride, out);
-            break;
-        case 2:
-            hipLaunchKernelGGL(reroute_kernel<2>, grid, dim3(2 * kWave), lds, s, ids, N, E, Phi,
-                               rho, sub, nsb, sps, nseg, ws, phy_quota, log2phy, logcnt, cp.flags, cp.bytes, cp.stride, out);
-            break;
-        default:
-            hipLaunchKernelGGL(reroute_kernel<1>, grid, dim3(kWave), lds, s, ids, N, E, Phi, rho,
-                               sub, nsb, sps, nseg, ws, phy_quota, log2phy, logcnt, cp.flags, cp.bytes, cp.stride, out);
-            break;
+    const bool bytes = cp.bytes != nullptr;
+#define EP_RR(WV, BY)                                                                                \
+    hipLaunchKernelGGL((reroute_kernel<WV, BY>), grid, dim3(WV * kWave), lds, s, ids, N, E, Phi, rho, \
+                       sub, nsb, sps, nseg, ws, phy_quota, log2phy, logcnt, cp.flags, cp.bytes,       \
+                       cp.stride, out)
+    if (bytes) {
+        if (w == 8) EP_RR(8, true); else if (w == 4) EP_RR(4, true); else if (w == 2) EP_RR(2, true); else EP_RR(1, true);
+    } else {
+        if (w == 8) EP_RR(8, false); else if (w == 4) EP_RR(4, false); else if (w == 2) EP_RR(2, false); else EP_RR(1, false);
     }
+#undef EP_RR
     return hipGetLastError();
 }
 
