@@ -48,8 +48,10 @@ inline Tables tables_of(const ep_layout_t &L) {
 // ---------------------------------------------------------------------------
 // Sub-blocks: the pairs of one plan are cut into consecutive sub-blocks, one
 // per wave in the reroute and the dispatch layout.  The size aims at ~8K waves
-// in a launch, keeps the count table under 1/4 byte per pair (>= 16 (E+1)
-// pairs), and is a power of two between 2048 and 4096.
+// in a launch (so a launch of one or a few plans gets small sub-blocks and
+// more waves), keeps the count table under 1/2 byte per pair with E <= 256
+// (>= 8 (E+1) pairs) and under 1/4 byte otherwise (>= 16 (E+1)), and is a
+// power of two between 1024 and 4096 unless that bound asks for more.
 //
 // Segments: the histogram gives each workgroup a segment of `sps`
 // consecutive sub-blocks, one per wave.  After counting, each wave stores the
@@ -72,7 +74,7 @@ inline Tables tables_of(const ep_layout_t &L) {
 #define EP_SUB_MAX 4096
 #endif
 #ifndef EP_SUB_MIN
-#define EP_SUB_MIN 2048
+#define EP_SUB_MIN 1024
 #endif
 #ifndef EP_SEG_SUBS
 #define EP_SEG_SUBS 8
@@ -81,7 +83,9 @@ constexpr int kSegSubs = EP_SEG_SUBS;  // sub-blocks per segment = waves per his
 inline int64_t sub_pairs(int64_t N, int32_t P, int32_t E) {
     const int64_t tw = EP_SUB_TARGET_WAVES;
     int64_t want = (N * (int64_t)P + tw - 1) / tw;
-    int64_t lo = 16 * (int64_t)(E + 1);
+    // at least 8 (E + 1) pairs when the IDs get a byte copy (E <= 256), else
+    // 16 (E + 1): the count table stays under 1/2 or 1/4 byte per pair
+    int64_t lo = (E <= 256 ? 8 : 16) * (int64_t)(E + 1);
     if (lo < EP_SUB_MIN) lo = EP_SUB_MIN;
     if (want < lo) want = lo;
     int64_t sub = EP_SUB_MIN;

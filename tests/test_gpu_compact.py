@@ -24,6 +24,20 @@ def dev():
     return torch.device("cuda:0")
 
 
+def _sub_pairs(N, P, E):
+    # the library's sub-block size: about 8192 waves per launch, a power of two
+    # from 1024 to 4096, and at least 8 (E + 1) pairs (16 (E + 1) above E = 256)
+    want = -(-N * P // 8192)
+    lo = max(1024, (8 if E <= 256 else 16) * (E + 1))
+    want = max(want, lo)
+    sub = 1024
+    while sub < want and sub < 4096:
+        sub *= 2
+    while sub < lo:
+        sub *= 2
+    return sub
+
+
 def _layout(E, R=64, spare=1):
     base, extra = divmod(E, R)
     nc = [base + (1 if r < extra else 0) for r in range(R)]
@@ -60,7 +74,7 @@ def test_clean_and_flagged_subblocks(dev, E):
     P, N = 3, 100_003          # ragged tail; N % 4 != 0, so plans 1 and 2 are not 16-byte aligned
     print(f"[compact] E={E} P={P} N={N}", flush=True)
     ids_h = _ids(P, N, E, 5 + E)
-    sub = 8192 if E >= 256 else 4096
+    sub = _sub_pairs(N, P, E)
     # padding and bad IDs in a few sub-blocks only; plan 1 stays clean
     for p, sb, k, v in [(0, 1, 17, -1), (0, 5, 4000, E), (0, 5, 4001, E + 3), (2, 0, 0, -2),
                         (2, (N - 1) // sub, (N - 1) % sub, -1)]:
@@ -76,14 +90,15 @@ def test_clean_and_flagged_subblocks(dev, E):
     _check(ids_h, E, lay_o, out, disp)
 
 
-@pytest.mark.parametrize("N", [8 * 8192, 5 * 8192 + 1500 + 3])
+@pytest.mark.parametrize("N", [16 * 4096, 10 * 4096 + 1500 + 3])
 def test_unaligned_ids_aligned_output(dev, N):
-    # N = 5 * 8192 + 1503: a last sub-block of one whole group, two whole
-    # tiles and a ragged tail; plan 1's rows change alignment
+    # 4096-pair sub-blocks; N = 10 * 4096 + 1503: a last sub-block of one whole
+    # group, one whole tile and a ragged tail; plan 1's rows change alignment
     E, P = 256, 2
+    assert _sub_pairs(N, P, E) == 4096
     print(f"[compact] unaligned ids E={E} P={P} N={N}", flush=True)
     ids_h = _ids(P, N, E, 11)
-    ids_h[1, 3 * 8192 + 99] = -1
+    ids_h[1, 3 * 4096 + 99] = -1
     nc, ne, sc = _layout(E)
     lay_o = oracle.Layout.of(E, 64, nc, ne, sc)
     lay = ep.Layout.create(E, nc, ne, sc, device=dev)
@@ -104,8 +119,10 @@ def test_byte_copy_and_flags_in_workspace(dev):
     # the workspace layout is internal, but its compact part must hold the IDs'
     # low bytes and one flag per sub-block; read it back through the size formula
     E, P, N = 128, 2, 3 * 4096 + 100
+    sub = _sub_pairs(N, P, E)
+    assert sub == 2048
     ids_h = _ids(P, N, E, 3)
-    ids_h[1, 4096 + 7] = -1
+    ids_h[1, sub + 7] = -1
     nc, ne, sc = _layout(E)
     lay = ep.Layout.create(E, nc, ne, sc, device=dev)
     ids = torch.from_numpy(ids_h).to(dev)
@@ -117,14 +134,16 @@ def test_byte_copy_and_flags_in_workspace(dev):
     # within a sub-block, each whole group of 1024 pairs (4 tiles of 64 lanes x
     # 4 pairs) is stored lane-major: byte 16 l + 4 t + k <- pair 256 t + 4 l + k
     want = ids_h.astype(np.uint8).copy()
-    for b0 in range(0, N, 4096):
-        n = min(4096, N - b0)
+    for b0 in range(0, N, sub):
+        n = min(sub, N - b0)
         for g in range(n // 1024):
             blk = ids_h[:, b0 + 1024 * g: b0 + 1024 * (g + 1)].astype(np.uint8).reshape(P, 4, 64, 4)
             want[:, b0 + 1024 * g: b0 + 1024 * (g + 1)] = blk.transpose(0, 2, 1, 3).reshape(P, 1024)
     np.testing.assert_array_equal(got, want)
-    nsb = (N + 4095) // 4096
+    nsb = (N + sub - 1) // sub
     rows = P * (nsb + (nsb + 7) // 8 + 1) * (E + 1) * 4
     f0 = (rows + 255) // 256 * 256
     flags = w[f0:f0 + P * nsb * 4].view(np.int32).reshape(P, nsb)
-    np.testing.assert_array_equal(flags, [[0, 0, 0, 0], [0, 1, 0, 0]])
+    want_flags = np.zeros((P, nsb), np.int32)
+    want_flags[1, 1] = 1
+    np.testing.assert_array_equal(flags, want_flags)

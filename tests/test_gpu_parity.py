@@ -372,28 +372,50 @@ def test_plan_kernel_paths(dev, R, E, max_sp):
 
 
 def test_reroute_many_split_experts_in_one_subblock(dev):
-    # 200 experts on 64 ranks with 3 spare slots each; experts 0..119 carry 60
-    # pairs, the rest 1: the whole plan (7280 pairs) is one sub-block and more
-    # than 64 replicated experts have a quota boundary inside it (the reroute
-    # keeps 64 of them in registers and the rest in LDS)
-    E, R = 200, 64
+    # 200 experts on 64 ranks with 3 spare slots each, and a plan built by hand:
+    # experts 0..119 get a replica in a spare slot of another rank and half of
+    # their 16 pairs each; the other 80 experts carry 1 pair.  The plan's 2000
+    # pairs fit one sub-block (2048 pairs at E = 200 and one plan), in which
+    # 120 experts have a quota boundary (the reroute keeps 64 of them in
+    # registers and the rest in LDS).
+    E, R, S = 200, 64, 3
     nc = [4] * 8 + [3] * 56
-    lay_o = oracle.Layout.of(E, R, nc, list(range(E)), [3] * R)
+    first = np.concatenate([[0], np.cumsum([n + S for n in nc])])
+    Phi = int(first[-1])
+    rho = min(R, 1 + S * R)
+    native = np.concatenate([first[r] + np.arange(nc[r]) for r in range(R)])  # expert e's native slot
+    rank_of = np.repeat(np.arange(R), nc)
+    cnt = np.where(np.arange(E) < 120, 16, 1)
+    q = np.zeros(Phi, np.int32)
+    l2p = np.full((E, rho), -1, np.int32)
+    lc = np.ones(E, np.int32)
+    used = np.zeros(R, np.int64)
+    for e in range(E):
+        if e < 120:
+            r = (rank_of[e] + 1 + e % 7) % R          # another rank with a free spare slot
+            while used[r] >= S or r == rank_of[e]:
+                r = (r + 1) % R
+            rs = first[r] + nc[r] + used[r]
+            used[r] += 1
+            a, b = sorted([native[e], rs])
+            l2p[e, :2] = [a, b]
+            lc[e] = 2
+            q[a], q[b] = 8, 8
+        else:
+            l2p[e, 0] = native[e]
+            q[native[e]] = cnt[e]
     rng = np.random.default_rng(21)
-    cnt = np.where(np.arange(E) < 120, 60, 1)
     ids = rng.permutation(np.repeat(np.arange(E), cnt)).astype(np.int32)[None]
-    ld, _ = oracle.histogram(ids[0], E)
-    pl = oracle.plan(ld, lay_o)
-    n_split = int(np.sum((pl.logcnt >= 2) & (ld > 0)))
-    print(f"[many-split] replicated experts = {n_split}", flush=True)
-    assert n_split > 64
-    lay = ep.Layout.create(E, nc, list(range(E)), [3] * R, device=dev)
+    assert ids.shape[1] <= 2048
+    lay = ep.Layout.create(E, nc, list(range(E)), [S] * R, device=dev)
+    assert lay.num_phys == Phi and lay.max_replicas == rho
     d_ids = torch.from_numpy(ids).to(dev)
     _, ws, _ = ep.ep_load_histogram(d_ids, lay)
-    phys = ep.ep_reroute(d_ids, lay, torch.from_numpy(pl.phy_quota[None]).to(dev),
-                         torch.from_numpy(pl.log2phy[None]).to(dev), torch.from_numpy(pl.logcnt[None]).to(dev), ws)
+    phys = ep.ep_reroute(d_ids, lay, torch.from_numpy(q[None]).to(dev), torch.from_numpy(l2p[None]).to(dev),
+                         torch.from_numpy(lc[None]).to(dev), ws)
     torch.cuda.synchronize()
-    ref, _ = oracle.reroute(ids[0], E, pl.phy_quota, pl.log2phy, pl.logcnt)
+    ref, unplaced = oracle.reroute(ids[0], E, q, l2p, lc)
+    assert unplaced == 0
     np.testing.assert_array_equal(_np(phys[0]), ref)
 
 
