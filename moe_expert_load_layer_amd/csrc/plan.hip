@@ -366,24 +366,28 @@ __global__ __launch_bounds__(kWave) void plan_kernel_lanes(const int32_t *__rest
             cdirty = edirty[ce];
             if (cnr < 0) cpk = nri[ce];
         }
-        const uint64_t key = valid ? (((uint64_t)(uint32_t)cq << 32) | inv((uint32_t)ce)) : 0;
-        // order of the candidates: count the larger keys
         const uint64_t vm = __ballot(valid);
-        int crank = 0;
-        for (uint64_t mm = vm; mm; mm &= mm - 1) {
-            const int j = __ffsll((long long)mm) - 1;
-            const uint64_t kj = (uint64_t)readlane_i64((int64_t)key, j);
-            crank += kj > key ? 1 : 0;
-        }
-        const int nc = __popcll(vm);
         // candidates worth a re-level: replicated and set in edirty
         const uint64_t relevel = __ballot(valid && cic >= 2 && cdirty != 0);
 
         bool committed = false;
         for (int pass = relevel ? 0 : 1; pass < 2 && !committed; pass++) {
-            for (int c = 0; c < nc && !committed; c++) {
-                const int cl = __ffsll((long long)__ballot(valid && crank == c)) - 1;
-                if (pass == 0 && !((relevel >> cl) & 1)) continue;
+            // the pass's candidates in descending (quota, -expert) order, each
+            // found when needed (most steps commit on the first one): the
+            // largest quota left, the lowest expert among equal quotas (the
+            // experts on one rank are distinct)
+            uint64_t left = pass == 0 ? relevel : vm;
+            while (left && !committed) {
+                const bool in = (left >> lane) & 1;
+                const int qmax = wave_max_i32(in ? cq : -1);
+                uint64_t tm = __ballot(in && cq == qmax);
+                if (tm & (tm - 1)) {
+                    const bool tie = (tm >> lane) & 1;
+                    const int emin = wave_min_i32(tie ? ce : 0x7fffffff);
+                    tm = __ballot(tie && ce == emin);
+                }
+                const int cl = __ffsll((long long)tm) - 1;
+                left &= ~(1ull << cl);
                 const int e = __builtin_amdgcn_readlane(ce, cl);
                 int nr = __builtin_amdgcn_readlane(cnr, cl);
                 int idx, T;
