@@ -359,8 +359,9 @@ __global__ __launch_bounds__(kWave) void plan_kernel_lanes(const int32_t *__rest
             if (lane == NPR + j) { ce = e; cq = q; }
         }
         const bool valid = ce >= 0 && cq > 0;
-        // LDS reads of the candidates (dirty flag; native rank and index of a
-        // replica's expert) go out before the ordering below, which hides them
+        // LDS reads of the candidates: dirty flag; native rank and index of a
+        // replica's expert (skipping them when no candidate is replicated
+        // measured slower: the extra ballot costs more than the read)
         int cdirty = 0, cpk = 0;
         if (valid) {
             cdirty = edirty[ce];
