@@ -29,8 +29,9 @@ namespace {
 #ifndef EP_RR_MAX_WAVES
 #define EP_RR_MAX_WAVES 8
 #endif
-// groups of the byte copy in flight per wave: a whole 4096-pair sub-block at
-// once (1 KiB per wave); one group ahead measured 15 % slower
+// groups of the byte copy in flight per wave: four (4096 pairs, 1 KiB per
+// wave: the whole sub-block in the batched launches); one group ahead measured
+// 15 % slower, eight (more registers) 8 % slower
 #ifndef EP_RR_PF_GROUPS
 #define EP_RR_PF_GROUPS 4
 #endif
