@@ -197,16 +197,30 @@ __global__ __launch_bounds__(W *kWave, 7) void reroute_kernel(
         }
     }
     __syncthreads();
+    // one thread per instance (an expert with many replicas would otherwise
+    // chain two dependent global reads per instance): its slot and quota, then
+    // per expert the running sum over its instances in LDS
+    {
+        const int total = E > 0 ? rfirst[E - 1] + rcnt[E - 1] : 0;
+        for (int k = threadIdx.x; k < total; k += W * kWave) {
+            // the expert owning instance k: the last e with rfirst[e] <= k
+            int lo = 0, hi = E - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (rfirst[mid] <= k) lo = mid; else hi = mid - 1;
+            }
+            const int s = log2phy[((int64_t)p * E + lo) * rho + (k - rfirst[lo])];
+            const bool ok = s >= 0 && s < Phi;
+            inst[k] = make_int2(ok ? phy_quota[(int64_t)p * Phi + s] : 0, ok ? s : -1);
+        }
+    }
+    __syncthreads();
     for (int e = threadIdx.x; e < E; e += W * kWave) {
         const int f = rfirst[e], n = rcnt[e];
-        const int32_t *row = log2phy + ((int64_t)p * E + e) * rho;
         int64_t acc = 0;
         for (int t = 0; t < n; t++) {
-            const int s = row[t];
-            const bool ok = s >= 0 && s < Phi;
-            acc += ok ? phy_quota[(int64_t)p * Phi + s] : 0;
-            const int32_t end = acc > 0x7fffffff ? 0x7fffffff : (acc < 0 ? 0 : (int32_t)acc);
-            inst[f + t] = make_int2(end, ok ? s : -1);
+            acc += inst[f + t].x;
+            inst[f + t].x = acc > 0x7fffffff ? 0x7fffffff : (acc < 0 ? 0 : (int32_t)acc);
         }
     }
     __syncthreads();
