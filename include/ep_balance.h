@@ -193,6 +193,9 @@ int ep_plan_quota(const int32_t *load, int32_t num_plans, const ep_layout_t *lay
  *   ws        the workspace filled by ep_load_histogram for these IDs
  *   phys_ids  device int32 [P][N] (written): physical slot, -1 for padding,
  *             invalid IDs and pairs beyond the expert's total quota
+ * phys_ids 4-byte aligned.  LDS bounds the shape: 16 E + 8 Phi + 256 bytes
+ * must fit 64 KiB (E = 2047 with Phi up to about 4000); otherwise, and for
+ * a ws smaller than ep_workspace_bytes(N, P, E), EP_ERR_INVALID_ARG.
  */
 int ep_reroute(const int32_t *topk_ids, int64_t pairs_per_plan, int32_t num_plans,
                const ep_layout_t *layout, const int32_t *phy_quota, const int32_t *log2phy,
