@@ -61,6 +61,36 @@ def test_fullsize_path(dev, name):
 
 
 @pytest.mark.parametrize("name", W.WORKLOAD_ORDER)
+def test_fullsize_single_layer(dev, name):
+    # one full-size plan per launch, as a forward pass without batching calls
+    # the path: the library then cuts the plan into smaller sub-blocks (2048
+    # pairs at E = 128) than in the batched launch; dispatch layout included
+    wl = W.get(name)
+    E = wl.num_experts
+    p0 = wl.num_plans - 1
+    ids = W.make_ids(wl, device=dev, plans=[p0])
+    print(f"[fullsize-1] {name}: plan {p0}, N={ids.shape[1]}", flush=True)
+    lay = ep.Layout.from_workload(wl, device=dev)
+    out = ep.run_path(ids, lay)
+    pl_g = out["plan"]
+    off, pos, src = ep.ep_dispatch_layout(ids, lay, pl_g.phy_quota, pl_g.log2phy, pl_g.logcnt, out["ws"])
+    torch.cuda.synchronize()
+    ids_h = ids.cpu().numpy()[0]
+    lay_o = oracle.Layout.from_workload(wl)
+    ld, _ = oracle.histogram(ids_h, E)
+    assert np.array_equal(out["load"][0].cpu().numpy(), ld)
+    pl = oracle.plan(ld, lay_o)
+    assert np.array_equal(pl_g.phy_quota[0].cpu().numpy(), pl.phy_quota)
+    assert np.array_equal(pl_g.log2phy[0].cpu().numpy(), pl.log2phy)
+    ph, _ = oracle.reroute(ids_h, E, pl.phy_quota, pl.log2phy, pl.logcnt)
+    assert np.array_equal(out["phys"][0].cpu().numpy(), ph)
+    ro, rp, rs, _ = oracle.dispatch(ids_h, E, pl.phy_quota, pl.log2phy, pl.logcnt)
+    assert np.array_equal(off[0].cpu().numpy().astype(np.int64), ro)
+    assert np.array_equal(pos[0].cpu().numpy(), rp)
+    assert np.array_equal(src[0].cpu().numpy(), rs)
+
+
+@pytest.mark.parametrize("name", W.WORKLOAD_ORDER)
 def test_fullsize_slot_fill(dev, name):
     wl = W.get(name)
     print(f"[fullsize-fill] {name}: E={wl.num_experts} S={wl.num_spare} bytes/expert={wl.bytes_per_expert}",
