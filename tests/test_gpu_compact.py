@@ -147,3 +147,25 @@ def test_byte_copy_and_flags_in_workspace(dev):
     want_flags = np.zeros((P, nsb), np.int32)
     want_flags[1, 1] = 1
     np.testing.assert_array_equal(flags, want_flags)
+
+
+@pytest.mark.parametrize("E", [1, 2, 64])
+@pytest.mark.parametrize("N", [1023, 1024, 1025, 2047, 4096 + 3])
+def test_small_expert_counts_and_group_edges(dev, E, N):
+    # one to a few experts, and plan lengths on both sides of the 1024-pair
+    # group and 256-pair tile edges of the byte copy; plan 1 all padding
+    P, R = 2, 2 if E < 64 else 16
+    rng = np.random.default_rng(E * 7919 + N)
+    ids_h = rng.integers(0, E, size=(P, N)).astype(np.int32)
+    ids_h[1, :] = -1
+    nc = [E - E // 2, E // 2] if R == 2 else [E // R] * R
+    ne = list(range(E))
+    sc = [1] * R
+    lay_o = oracle.Layout.of(E, R, nc, ne, sc)
+    lay = ep.Layout.create(E, nc, ne, sc, device=dev)
+    ids = torch.from_numpy(ids_h).to(dev)
+    out = ep.run_path(ids, lay)
+    pl = out["plan"]
+    disp = ep.ep_dispatch_layout(ids, lay, pl.phy_quota, pl.log2phy, pl.logcnt, out["ws"])
+    torch.cuda.synchronize()
+    _check(ids_h, E, lay_o, out, disp)
