@@ -310,6 +310,7 @@ __global__ __launch_bounds__(kWave) void plan_kernel_lanes(const int32_t *__rest
     const int32_t *lp = load + (int64_t)p * E;
 
     const bool is_rank = lane < R;
+    const uint64_t rank_mask = R >= kWave ? ~0ull : ((1ull << R) - 1);
     const int f0 = is_rank ? a.T.rank_first[lane] : 0;
     const int nat = is_rank ? a.T.rank_nat[lane] : 0;
     const int spc = is_rank ? a.T.rank_first[lane + 1] - f0 - nat : 0;
@@ -339,7 +340,9 @@ __global__ __launch_bounds__(kWave) void plan_kernel_lanes(const int32_t *__rest
         if (steps == cap) { cap_hit = 1; break; }
         // hottest rank (lowest index on ties)
         const int vmax = wave_max_i32(is_rank ? rl : -1);
-        const int h = __ffsll((long long)__ballot(is_rank && rl == vmax)) - 1;
+        // (a ballot of one compare, masked in scalar registers, saves turning
+        // a combined condition into a vector value and back)
+        const int h = __ffsll((long long)(__ballot(rl == vmax) & rank_mask)) - 1;
         const int Lh = vmax;
 
         // candidates: h's natives in lanes [0, NPR), h's spare slots in [NPR, NPR+SPR)
@@ -381,11 +384,11 @@ __global__ __launch_bounds__(kWave) void plan_kernel_lanes(const int32_t *__rest
             while (left && !committed) {
                 const bool in = (left >> lane) & 1;
                 const int qmax = wave_max_i32(in ? cq : -1);
-                uint64_t tm = __ballot(in && cq == qmax);
+                uint64_t tm = __ballot(cq == qmax) & left;
                 if (tm & (tm - 1)) {
                     const bool tie = (tm >> lane) & 1;
                     const int emin = wave_min_i32(tie ? ce : 0x7fffffff);
-                    tm = __ballot(tie && ce == emin);
+                    tm &= __ballot(ce == emin);
                 }
                 const int cl = __ffsll((long long)tm) - 1;
                 left &= ~(1ull << cl);
