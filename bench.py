@@ -224,7 +224,17 @@ def main(argv=None) -> int:
 
     st = stats.cpu().numpy()
     used = st[:, 3]
-    fill_bytes = 2.0 * bpe * used                       # per layer (launch)
+    # algorithmic bytes of one slot fill: the weights of every distinct expert
+    # among the filled spare slots read once, every filled slot written once
+    # (an expert replicated into k slots of a layer is read once, written k times)
+    spare_idx, s0 = [], 0
+    for nc_r, sc_r in zip(wl.native_count, wl.spare_count):
+        s0 += int(nc_r)
+        spare_idx.extend(range(s0, s0 + int(sc_r)))
+        s0 += int(sc_r)
+    sp = plan.phy2log.cpu().numpy()[:, spare_idx]
+    distinct = np.array([len(np.unique(r[r >= 0])) for r in sp], np.float64)
+    fill_bytes = bpe * (distinct + used)                # per layer (launch)
     fill_ms = np.array(ms["fill"]).reshape(args.steps, P).mean(axis=0)
     fill_gbps = float(fill_bytes.mean() / (fill_ms.mean() * 1e-3) / 1e9)
     imb_np = imb.cpu().numpy()
@@ -344,6 +354,8 @@ def main(argv=None) -> int:
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": fill_gbps / HBM_PEAK_GBPS,
                      "traffic": traffic,
                      "bytes_per_launch": float(fill_bytes.mean()),
+                     "bytes_rule": "(distinct experts in filled spare slots + filled slots) x bytes_per_expert",
+                     "filled_slots_mean": float(used.mean()), "distinct_experts_mean": float(distinct.mean()),
                      "launch_ms": float(fill_ms.mean())},
         "phases_ms_per_step": {"path": path_ms, "stats": statistics.mean(ms["stats"]),
                                "fill": float(fill_ms.sum())},

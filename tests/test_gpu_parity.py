@@ -260,6 +260,30 @@ def test_slot_fill_with_oracle_plan(dev, name):
         np.testing.assert_array_equal(_np(buf.view(torch.int16)), ref)
 
 
+@pytest.mark.parametrize("S", [8, 300, 1024, 1025])
+def test_slot_fill_replicated_experts(dev, S):
+    # a few experts fill most spare slots (each read once for all its slots
+    # up to 1024 spare slots, slot by slot above), some slots empty; rows of
+    # two whole 16 KiB chunks and a tail
+    E, R = 16, 16
+    nc, ne = [1] * R, list(range(E))
+    sc = [S // R + (1 if r < S % R else 0) for r in range(R)]
+    lay = ep.Layout.create(E, nc, ne, sc, device=dev)
+    lay_o = oracle.Layout.of(E, R, nc, ne, sc)
+    first, home, rank, spare = lay_o.slots()
+    rng = np.random.default_rng(S)
+    phy2log = home.astype(np.int32).copy()
+    phy2log[spare] = rng.choice([-1, 0, 1, 2, 3, 15], size=S, p=[0.2, 0.3, 0.2, 0.1, 0.1, 0.1])
+    elems = 2 * 8192 + 40                               # bf16: 2 chunks of 16 KiB + 80 bytes
+    w = rng.integers(0, 1 << 16, size=(E, elems), dtype=np.uint16)
+    ref = np.full((S, elems), 0x7FC1, np.uint16)
+    oracle.slot_fill(w, phy2log, lay_o, ref)
+    buf = torch.from_numpy(np.full((S, elems), 0x7FC1, np.uint16).view(np.int16)).to(dev)
+    ep.ep_slot_fill(torch.from_numpy(w.view(np.int16)).to(dev), torch.from_numpy(phy2log).to(dev), lay, buf)
+    torch.cuda.synchronize()
+    assert np.array_equal(buf.cpu().numpy().view(np.uint16), ref)
+
+
 # --------------------------------------------------------------------- A5
 @pytest.mark.parametrize("name", W.WORKLOAD_ORDER)
 def test_stats_with_oracle_inputs(dev, name):
