@@ -44,7 +44,7 @@ METRIC = "(token,k) pairs/s via hist+plan+reroute; plan µs/layer at EP64; HBM G
 # HBM bytes per slot-fill launch measured with rocprofv3 --pmc (FETCH_SIZE and
 # WRITE_SIZE), scaled by the same counters on a plain copy of known size; valid
 # only for the kernel source they were taken on.
-TRAFFIC = {"kernel_sha": "f464a1ef3130fe8f", "fetch_kib": 1145029.5, "write_kib": 2290666.3, "fetch_scale": 2.0, "write_scale": 1.0, "bytes_per_launch": 4690662837}
+TRAFFIC = {"kernel_sha": "98e1c4c10e601569", "fetch_kib": 483585.7, "write_kib": 2290701.0, "fetch_scale": 2.0, "write_scale": 1.0, "bytes_per_launch": 3336061381}
 
 
 def _src_sha(name: str) -> str:
@@ -350,7 +350,7 @@ def main(argv=None) -> int:
                                f"{wl.tokens_per_rank} tokens/rank, {P} layers, {S} spare slots, "
                                f"expert 3x4096x1536 bf16",
                    "pairs_per_step": P * N, "plans_per_step": P},
-        "roofline": {"bound": "hbm", "kernel": "slot_fill_kernel", "achieved": fill_gbps,
+        "roofline": {"bound": "hbm", "kernel": "slot_fill_shared_kernel", "achieved": fill_gbps,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": fill_gbps / HBM_PEAK_GBPS,
                      "traffic": traffic,
                      "bytes_per_launch": float(fill_bytes.mean()),

