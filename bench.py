@@ -237,6 +237,9 @@ def main(argv=None) -> int:
     fill_bytes = bpe * (distinct + used)                # per layer (launch)
     fill_ms = np.array(ms["fill"]).reshape(args.steps, P).mean(axis=0)
     fill_gbps = float(fill_bytes.mean() / (fill_ms.mean() * 1e-3) / 1e9)
+    # the rate at which slot rows are filled, counted as a copy per slot would
+    # move them (read + write per filled slot); not HBM bytes
+    fill_eff_gbps = float((2 * bpe * used).mean() / (fill_ms.mean() * 1e-3) / 1e9)
     imb_np = imb.cpu().numpy()
 
     # single-plan latencies (one layer, as a real forward pass sees them)
@@ -356,6 +359,7 @@ def main(argv=None) -> int:
                      "bytes_per_launch": float(fill_bytes.mean()),
                      "bytes_rule": "(distinct experts in filled spare slots + filled slots) x bytes_per_expert",
                      "filled_slots_mean": float(used.mean()), "distinct_experts_mean": float(distinct.mean()),
+                     "per_slot_copy_equivalent_GBps": fill_eff_gbps,
                      "launch_ms": float(fill_ms.mean())},
         "phases_ms_per_step": {"path": path_ms, "stats": statistics.mean(ms["stats"]),
                                "fill": float(fill_ms.sum())},
