@@ -47,6 +47,21 @@ METRIC = "(token,k) pairs/s via hist+plan+reroute; plan µs/layer at EP64; HBM G
 TRAFFIC = {"kernel_sha": "98e1c4c10e601569", "fetch_kib": 483585.7, "write_kib": 2290701.0, "fetch_scale": 2.0, "write_scale": 1.0, "bytes_per_launch": 3336061381}
 
 
+def _sub_pairs(N: int, P: int, E: int) -> int:
+    """The library's sub-block size for P plans of N pairs: about 8192 waves per
+    launch, a power of two from 1024 to 4096 pairs, and at least 8 (E + 1) pairs
+    (16 (E + 1) above 256 experts)."""
+    want = -(-N * P // 8192)
+    lo = max(1024, (8 if E <= 256 else 16) * (E + 1))
+    want = max(want, lo)
+    sub = 1024
+    while sub < want and sub < 4096:
+        sub *= 2
+    while sub < lo:
+        sub *= 2
+    return sub
+
+
 def _src_sha(name: str) -> str:
     with open(os.path.join(ROOT, "moe_expert_load_layer_amd", "csrc", name), "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -283,6 +298,14 @@ def main(argv=None) -> int:
     # one-byte copy of each ID (4 in, 1 out), which the reroute reads instead
     # of the int32 ID (1 in, 4 out); otherwise 4 in, and 4 in + 4 out
     hist_bpp, rr_bpp = (5.0, 5.0) if E <= 256 else (4.0, 8.0)
+    # plus the per-sub-block counts the histogram hands to the reroute: one
+    # row of E + 1 int32 per sub-block (in-segment prefixes and segment
+    # totals), written by the histogram and read by the reroute (a sub-block's
+    # rank ranges end where the next one's start)
+    sub = _sub_pairs(N, P, E)
+    rows_pp = -(-N // sub) * (E + 1) * 4 / N
+    hist_bpp += rows_pp
+    rr_bpp += rows_pp
     hist_gbps = hist_bpp * P * N / (ph_hist * 1e-3) / 1e9
     rr_gbps = rr_bpp * P * N / (ph_rr * 1e-3) / 1e9
 

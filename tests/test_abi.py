@@ -116,3 +116,22 @@ def test_entry_points_reject_unsupported_shapes_on_host():
     # gradient rows must be a multiple of 4 floats
     rc = L.ep_replica_grad_reduce(fake, 6, fake, fake, fake, ctypes.byref(lay), None)
     assert rc == ep.EP_ERR_INVALID_ARG
+
+
+def test_bench_sub_block_rule_matches_the_library():
+    # bench.py counts the histogram's count rows with its own copy of the
+    # sub-block rule; the library's workspace size pins it
+    import bench
+    import moe_expert_load_layer_amd as ep
+    if not os.path.exists(ep.LIB_PATH):
+        pytest.skip("library not built")
+    a = lambda x: (x + 255) // 256 * 256
+    for N, P, E in [(4194304, 256, 384), (4194304, 94, 300), (100003, 3, 257), (1 << 20, 1, 300),
+                    (5, 2, 1000), (4194304, 94, 128), (2097152, 58, 256), (5242880, 92, 160),
+                    (4194304, 47, 128), (1000, 1, 12)]:
+        sub = bench._sub_pairs(N, P, E)
+        nsb = -(-N // sub)
+        nseg = -(-nsb // 8)
+        rows = P * (nsb + nseg + 1) * (E + 1) * 4
+        want = a(rows) + a(P * nsb * 4) + P * ((N + 15) // 16 * 16) if E <= 256 else rows
+        assert ep.ep_workspace_bytes(N, P, E) == want, (N, P, E)
