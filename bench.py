@@ -62,6 +62,17 @@ def _sub_pairs(N: int, P: int, E: int) -> int:
     return sub
 
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def _src_sha(name: str) -> str:
     with open(os.path.join(ROOT, "moe_expert_load_layer_amd", "csrc", name), "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -454,6 +465,7 @@ def main(argv=None) -> int:
             out["balance"]["imbalance_lower_bound_mean"] = float(lb[:, 0].mean())
             out["balance"]["imbalance_after_over_bound_max"] = float((lb[:, 1] / lb[:, 0]).max())
         cb["host_threads_available"] = os.cpu_count()
+        cb["host_cpu"] = _cpu_model()
     else:
         out["cpu_baseline"] = None
 
