@@ -234,7 +234,8 @@ int ep_dispatch_layout(const int32_t *topk_ids, int64_t pairs_per_plan, int32_t 
  *   expert_weights device [E][bytes_per_expert], one layer (16-byte aligned)
  *   phy2log        device int32 [Phi], that layer's plan
  *   slot_buf       device [S][bytes_per_expert] (16-byte aligned)
- * bytes_per_expert must be a positive multiple of 16.
+ * bytes_per_expert must be a positive multiple of 16.  A spare slot whose
+ * phy2log entry lies outside [0, E) is empty: its row is not written.
  */
 int ep_slot_fill(const void *expert_weights, int64_t bytes_per_expert, const int32_t *phy2log,
                  const ep_layout_t *layout, void *slot_buf, ep_stream_t stream);

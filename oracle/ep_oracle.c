@@ -366,7 +366,7 @@ int or_slot_fill(const uint8_t *weights, int64_t bytes_per_expert, int32_t E, in
     if (rc != OR_OK) return rc;
     for (int o = 0; o < L.S; o++) {
         int e = phy2log[L.spare_slot[o]];
-        if (e < 0) continue;
+        if (e < 0 || e >= E) continue; /* not an expert: an empty slot (R15) */
         memcpy(slot_buf + (int64_t)o * bytes_per_expert, weights + (int64_t)e * bytes_per_expert,
                (size_t)bytes_per_expert);
     }

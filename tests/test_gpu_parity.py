@@ -284,6 +284,29 @@ def test_slot_fill_replicated_experts(dev, S):
     assert np.array_equal(buf.cpu().numpy().view(np.uint16), ref)
 
 
+@pytest.mark.parametrize("S", [8, 1025])
+def test_slot_fill_entries_naming_no_expert(dev, S):
+    # spare entries outside [0, E) (E, E + 7, INT32_MAX) name no expert: their
+    # rows keep the sentinel, in the shared fill (S <= 1024) and the per-slot one
+    E, R = 16, 16
+    nc, ne = [1] * R, list(range(E))
+    sc = [S // R + (1 if r < S % R else 0) for r in range(R)]
+    lay = ep.Layout.create(E, nc, ne, sc, device=dev)
+    lay_o = oracle.Layout.of(E, R, nc, ne, sc)
+    first, home, rank, spare = lay_o.slots()
+    rng = np.random.default_rng(100 + S)
+    phy2log = home.astype(np.int32).copy()
+    phy2log[spare] = rng.choice([-1, 0, 5, 15, E, E + 7, 2 ** 31 - 1], size=S)
+    elems = 8192 + 24
+    w = rng.integers(0, 1 << 16, size=(E, elems), dtype=np.uint16)
+    ref = np.full((S, elems), 0x7FC1, np.uint16)
+    oracle.slot_fill(w, phy2log, lay_o, ref)
+    buf = torch.from_numpy(np.full((S, elems), 0x7FC1, np.uint16).view(np.int16)).to(dev)
+    ep.ep_slot_fill(torch.from_numpy(w.view(np.int16)).to(dev), torch.from_numpy(phy2log).to(dev), lay, buf)
+    torch.cuda.synchronize()
+    assert np.array_equal(buf.cpu().numpy().view(np.uint16), ref)
+
+
 # --------------------------------------------------------------------- A5
 @pytest.mark.parametrize("name", W.WORKLOAD_ORDER)
 def test_stats_with_oracle_inputs(dev, name):

@@ -80,3 +80,15 @@ def test_slot_fill_leaves_empty_slots():
     assert buf[0].tolist() == [0xEE] * 8
     assert buf[1].tolist() == w[0].tolist()
     assert buf[2].tolist() == [0xEE] * 8
+
+
+def test_slot_fill_entries_that_name_no_expert_are_empty():
+    # a phy2log entry outside [0, E) names no expert: that spare slot is empty
+    lay = oracle.Layout.of(3, 2, [2, 1], [0, 1, 2], [1, 2])
+    w = np.arange(3 * 8, dtype=np.uint8).reshape(3, 8)
+    buf = np.full((3, 8), 0xEE, np.uint8)
+    phy2log = np.array([0, 1, 3, 2, 2, 2 ** 31 - 1], np.int32)  # spares: E, expert 2, INT32_MAX
+    oracle.slot_fill(w, phy2log, lay, buf)
+    assert buf[0].tolist() == [0xEE] * 8
+    assert buf[1].tolist() == w[2].tolist()
+    assert buf[2].tolist() == [0xEE] * 8
