@@ -199,11 +199,15 @@ __global__ __launch_bounds__(W *kWave) void dispatch_kernel(
     const uint32_t uE = (uint32_t)E;
     constexpr int U = 8;
     // the IDs of the next U columns load while the current ones are ranked
+    // (the loads are unconditional, from a clamped index, so that the wait
+    // for a group's IDs does not also wait for the next group's)
+    const int64_t last = end - 1;
     int32_t nxt[U];
 #pragma unroll
     for (int u = 0; u < U; u++) {
         const int64_t i = begin + u * kWave + lane;
-        nxt[u] = i < end ? __builtin_nontemporal_load(src + i) : -1;
+        const int32_t t = __builtin_nontemporal_load(src + (i < end ? i : last));
+        nxt[u] = i < end ? t : -1;
     }
     for (int64_t g = begin; g < end; g += U * kWave) {
         int32_t v[U];
@@ -211,7 +215,8 @@ __global__ __launch_bounds__(W *kWave) void dispatch_kernel(
         for (int u = 0; u < U; u++) {
             v[u] = nxt[u];
             const int64_t i = g + (U + u) * kWave + lane;
-            nxt[u] = i < end ? __builtin_nontemporal_load(src + i) : -1;
+            const int32_t t = __builtin_nontemporal_load(src + (i < end ? i : last));
+            nxt[u] = i < end ? t : -1;
         }
 #pragma unroll
         for (int u = 0; u < U; u++) {
