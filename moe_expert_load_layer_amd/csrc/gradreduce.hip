@@ -24,7 +24,12 @@ __global__ __launch_bounds__(kRedThreads) void grad_reduce_kernel(
     f32x4 *__restrict__ native, int64_t vpe, const f32x4 *__restrict__ slot,
     const int32_t *__restrict__ log2phy, const int32_t *__restrict__ logcnt, int32_t rho,
     int32_t Phi, Tables T) {
-    __shared__ const f32x4 *rows[64];
+    // instance rows as codes: h >= 0 the native row of expert h, -1 - o the
+    // o-th spare slot's row, kNoRow not a plan's table (codes rather than
+    // pointers: a pointer read back from LDS is generic, and its loads would
+    // be flat ones, which the LDS wait counter also tracks)
+    constexpr int32_t kNoRow = INT32_MIN;
+    __shared__ int32_t rows[64];
     const int e = blockIdx.y;
     int c = logcnt[e];
     c = c > rho ? rho : c;
@@ -35,39 +40,62 @@ __global__ __launch_bounds__(kRedThreads) void grad_reduce_kernel(
         const bool ok = s >= 0 && s < Phi;
         const int home = ok ? T.slot_home[s] : -1;
         const int o = ok ? T.slot_spare[s] : -1;
-        rows[threadIdx.x] = home >= 0 ? native + (int64_t)home * vpe
-                                      : (o >= 0 ? slot + (int64_t)o * vpe : nullptr);
+        rows[threadIdx.x] = home >= 0 ? home : (o >= 0 ? -1 - o : kNoRow);
     }
     __syncthreads();
     for (int t = 0; t < c; t++)
-        if (rows[t] == nullptr) return;   // not a plan's table: leave the row alone
+        if (rows[t] == kNoRow) return;   // not a plan's table: leave the row alone
     const int64_t c0 = (int64_t)blockIdx.x * kRedChunk;
     const int64_t c1 = (c0 + kRedChunk < vpe) ? c0 + kRedChunk : vpe;
     f32x4 *out = native + (int64_t)e * vpe;
-    // all kRedIters vectors of a thread load together for each row (more
-    // loads in flight), non-temporal as every byte is touched once; each
-    // element still folds its rows in slot order
-    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-    f32x4 acc[kRedIters];
+    auto row = [&](int t) -> const f32x4 * {
+        const int32_t r = rows[t];
+        return r >= 0 ? native + (int64_t)r * vpe : slot + (int64_t)(-1 - r) * vpe;
+    };
+    // all kRedIters vectors of a thread load together, two rows per step (more
+    // loads in flight), non-temporal as every byte is touched once.  The loads
+    // are unconditional, from an index clamped to the chunk, so that the wait
+    // for one row does not also wait for the other; lanes past the chunk's end
+    // fold whatever they read and store nothing.  Each element still folds its
+    // rows in slot order, one fp32 add at a time.
+    int64_t idx[kRedIters];
 #pragma unroll
     for (int k = 0; k < kRedIters; k++) {
         const int64_t i = c0 + threadIdx.x + k * kRedThreads;
-        acc[k] = i < c1 ? __builtin_nontemporal_load(rows[0] + i) : zero;
+        idx[k] = i < c1 ? i : c1 - 1;
     }
-    for (int t = 1; t < c; t++) {
-        f32x4 g[kRedIters];
+    f32x4 acc[kRedIters];
+    {
+        const f32x4 *r0 = row(0);
 #pragma unroll
-        for (int k = 0; k < kRedIters; k++) {
-            const int64_t i = c0 + threadIdx.x + k * kRedThreads;
-            g[k] = i < c1 ? __builtin_nontemporal_load(rows[t] + i) : zero;
-        }
+        for (int k = 0; k < kRedIters; k++) acc[k] = __builtin_nontemporal_load(r0 + idx[k]);
+    }
+    auto add = [&](f32x4 &a, const f32x4 &g) {
+        a.x = a.x + g.x;
+        a.y = a.y + g.y;
+        a.z = a.z + g.z;
+        a.w = a.w + g.w;
+    };
+    int t = 1;
+    for (; t + 1 < c; t += 2) {
+        const f32x4 *ra = row(t), *rb = row(t + 1);
+        f32x4 ga[kRedIters], gb[kRedIters];
 #pragma unroll
-        for (int k = 0; k < kRedIters; k++) {
-            acc[k].x = acc[k].x + g[k].x;
-            acc[k].y = acc[k].y + g[k].y;
-            acc[k].z = acc[k].z + g[k].z;
-            acc[k].w = acc[k].w + g[k].w;
-        }
+        for (int k = 0; k < kRedIters; k++) ga[k] = __builtin_nontemporal_load(ra + idx[k]);
+#pragma unroll
+        for (int k = 0; k < kRedIters; k++) gb[k] = __builtin_nontemporal_load(rb + idx[k]);
+#pragma unroll
+        for (int k = 0; k < kRedIters; k++) add(acc[k], ga[k]);
+#pragma unroll
+        for (int k = 0; k < kRedIters; k++) add(acc[k], gb[k]);
+    }
+    if (t < c) {
+        const f32x4 *ra = row(t);
+        f32x4 ga[kRedIters];
+#pragma unroll
+        for (int k = 0; k < kRedIters; k++) ga[k] = __builtin_nontemporal_load(ra + idx[k]);
+#pragma unroll
+        for (int k = 0; k < kRedIters; k++) add(acc[k], ga[k]);
     }
 #pragma unroll
     for (int k = 0; k < kRedIters; k++) {
