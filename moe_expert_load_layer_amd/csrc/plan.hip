@@ -278,12 +278,14 @@ __global__ __launch_bounds__(kWave) void plan_kernel_generic(const int32_t *__re
 // the re-level pass), and, at the end, the per-expert masks of replica ranks
 // used to order log2phy.
 // ---------------------------------------------------------------------------
+// v[i] (v[0] for i outside [0, N)) from registers.  Built from masks rather
+// than selects: the compiler turns a chain of selects between elements into
+// one indexed load, which keeps the whole array in scratch memory.
 template <int N>
 __device__ __forceinline__ int32_t pick(const int32_t (&v)[N], int i) {
-    int32_t r = v[0];
+    int32_t r = v[0] & -(int32_t)(i < 1 || i >= N);
 #pragma unroll
-    for (int k = 1; k < N; k++)
-        if (i == k) r = v[k];
+    for (int k = 1; k < N; k++) r |= v[k] & -(int32_t)(i == k);
     return r;
 }
 
@@ -454,9 +456,13 @@ __global__ __launch_bounds__(kWave) void plan_kernel_lanes(const int32_t *__rest
                 // commit (lane-local)
                 if (act) rl = b + qn;
                 if (nat_here) {
+                    // (value selects, not stores under a condition, for the
+                    // same reason as in pick)
 #pragma unroll
-                    for (int i = 0; i < NPR; i++)
-                        if (i == idx) { nat_q[i] = qn; if (replicate) nat_ic[i] += 1; }
+                    for (int i = 0; i < NPR; i++) {
+                        nat_q[i] = i == idx ? qn : nat_q[i];
+                        nat_ic[i] += (i == idx && replicate) ? 1 : 0;
+                    }
                 }
 #pragma unroll
                 for (int j = 0; j < SPR; j++)
