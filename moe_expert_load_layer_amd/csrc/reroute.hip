@@ -153,11 +153,12 @@ __device__ __forceinline__ void resolve_split(const int32_t (&x)[K], int32_t (&c
     }
 }
 
-// At most 72 VGPRs (7 waves per SIMD; the compiler moves a few values of the
-// rare split path to scratch): 5 % faster than the 78 it picks unbounded, at
-// 8 waves (64 VGPRs) the spills cost more than the waves gain.
+// Reading the byte copy: at most 72 VGPRs (7 waves per SIMD; the compiler
+// moves a few values of the rare split path to scratch), 5 % faster than the
+// 78 it picks unbounded; at 8 waves (64 VGPRs) the spills cost more than the
+// waves gain.  Reading int32 IDs the bound costs 2 %, so it is not set there.
 template <int W, bool BYTES>
-__global__ __launch_bounds__(W *kWave, 7) void reroute_kernel(
+__global__ __launch_bounds__(W *kWave, BYTES ? 7 : 1) void reroute_kernel(
     const int32_t *__restrict__ ids, int64_t N, int32_t E, int32_t Phi, int32_t rho, int64_t sub,
     int64_t nsb, int64_t sps, int64_t nseg, const int32_t *__restrict__ ws, const int32_t *__restrict__ phy_quota,
     const int32_t *__restrict__ log2phy, const int32_t *__restrict__ logcnt,
