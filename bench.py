@@ -14,10 +14,11 @@ Inputs are synthetic, seeded, and resident in HBM before timing starts.
 value = (token,k) pairs per second through hist + plan + reroute (HIP events
 around that phase in every timed step); ms_per_step is the whole step
 including the slot fills and statistics.  The roofline object covers the
-dominant kernel (slot fill): algorithmic bytes = 2 * bytes_per_expert per
-filled spare slot, divided by the mean launch time from HIP events on the
-stream the kernel runs on.  The CPU baseline times the C oracle on a bounded
-sample of the same layers on the host.
+dominant kernel (slot fill): algorithmic bytes = (distinct experts among the
+filled spare slots + filled slots) * bytes_per_expert (each replicated expert
+read once, each slot written once), divided by the mean launch time from HIP
+events on the stream the kernel runs on.  The CPU baseline times the C oracle
+on a bounded sample of the same layers on the host.
 """
 from __future__ import annotations
 
