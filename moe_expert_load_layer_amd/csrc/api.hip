@@ -173,7 +173,7 @@ int ep_dispatch_layout(const int32_t *topk_ids, int64_t N, int32_t P, const ep_l
     if (N > 0 && (!dispatch_pos || !dispatch_src || !aligned(dispatch_pos, 4) || !aligned(dispatch_src, 4)))
         return EP_ERR_INVALID_ARG;
     const int E = layout->num_experts;
-    if (dispatch_lds_bytes(E, layout->num_phys, 1, 0) > kMaxLds) return EP_ERR_INVALID_ARG;
+    if (dispatch_lds_bytes(E, layout->num_phys, 1, 0, false) > kMaxLds) return EP_ERR_INVALID_ARG;
     const size_t need = ws_bytes(N, P, E);
     if (ws_size < need || (need > 0 && (!ws || !aligned(ws, 16)))) return EP_ERR_INVALID_ARG;
     return hip_rc(launch_dispatch(topk_ids, N, P, *layout, sub_geom(N, P, E), static_cast<const int32_t *>(ws), phy_quota, log2phy, logcnt,

@@ -22,6 +22,8 @@
 // then writes the staged slots in order, 64 at a time; a cell's pairs go to
 // consecutive positions, so each store writes a few coalesced runs.
 // Otherwise each pair's index is stored at its position directly.
+#include <type_traits>
+
 #include "ep_internal.h"
 
 namespace ep {
@@ -33,11 +35,27 @@ namespace {
 // the one instance that takes all of the expert's pairs here, or the run
 // itself when a quota boundary falls inside (split), so that the k-th pair
 // of the cell goes to base + k, or to the instance a search of run + k finds.
-struct Cell {
+struct Cell1 {
     uint64_t mask;
     uint32_t kf;
     int32_t base;
 };
+// ranking two columns per LDS round trip keeps a mask per column
+struct Cell2 {
+    uint64_t mask;   // lanes of the first column of the current pair
+    uint64_t mask1;  // lanes of the second column
+    uint32_t kf;
+    int32_t base;
+};
+template <bool PAIR> using CellOf = typename std::conditional<PAIR, Cell2, Cell1>::type;
+template <bool PAIR> __device__ __forceinline__ CellOf<PAIR> make_cell(uint32_t kf, int32_t base) {
+    CellOf<PAIR> c;
+    c.mask = 0ull;
+    if constexpr (PAIR) c.mask1 = 0ull;
+    c.kf = kf;
+    c.base = base;
+    return c;
+}
 constexpr uint32_t kSplitFlag = 1u << 30;  // a quota boundary falls inside the cell
 constexpr uint32_t kNoneFlag = 1u << 31;   // no instance takes these pairs
 constexpr uint32_t kCountMask = kSplitFlag - 1;
@@ -52,7 +70,7 @@ __device__ __forceinline__ int32_t position_of(const int2 *inst, int f, int n, i
     return -1;
 }
 
-template <int W, bool STAGED>
+template <int W, bool STAGED, bool PAIR>
 __global__ __launch_bounds__(W *kWave) void dispatch_kernel(
     const int32_t *__restrict__ ids, int64_t N, int32_t E, int32_t Phi, int32_t rho, int64_t sub,
     int64_t nsb, int64_t sps, int64_t nseg, const int32_t *__restrict__ ws, const int32_t *__restrict__ phy_quota,
@@ -62,6 +80,7 @@ __global__ __launch_bounds__(W *kWave) void dispatch_kernel(
     const int64_t nwords = STAGED ? sub / kWave : 0;                         // cell-start bit words
     const int E1c = E + 1;                                                  // cell E: padding, bad IDs
     const int64_t sstride = STAGED ? sub + kWave : 0;                       // slot sub: sink
+    using Cell = CellOf<PAIR>;
     Cell *cell_all = reinterpret_cast<Cell *>(sh_raw);                      // [W][E+1]
     uint64_t *sbits_all = reinterpret_cast<uint64_t *>(cell_all + (size_t)W * E1c); // [W][sub/64] if STAGED
     int2 *inst = reinterpret_cast<int2 *>(sbits_all + (size_t)W * nwords);  // [Phi] (end, off - Q)
@@ -169,7 +188,7 @@ __global__ __launch_bounds__(W *kWave) void dispatch_kernel(
             const int incl = wave_incl_scan_i32(cnt);
             const int off = carry + incl - cnt;
             if (e < E) {
-                cells[e] = Cell{0ull, flags, base};
+                cells[e] = make_cell<PAIR>(flags, base);
                 if (STAGED) offs[e] = off;
             }
             if (STAGED) {
@@ -185,7 +204,7 @@ __global__ __launch_bounds__(W *kWave) void dispatch_kernel(
             carry += __shfl(incl, kWave - 1);
         }
         staged_pairs = carry;
-        if (lane == 0) cells[E] = Cell{0ull, kNoneFlag, 0};
+        if (lane == 0) cells[E] = make_cell<PAIR>(kNoneFlag, 0);
     }
     wave_lds_fence();
 
@@ -218,26 +237,70 @@ __global__ __launch_bounds__(W *kWave) void dispatch_kernel(
             const int32_t t = __builtin_nontemporal_load(src + (i < end ? i : last));
             nxt[u] = i < end ? t : -1;
         }
+        if constexpr (PAIR) {
+            // two columns per LDS round trip: each ORs its lanes into its own
+            // mask of the expert's cell, one read then ranks both (a pair in the
+            // second column also counts all of its expert's pairs in the first),
+            // and the expert's first lane in the pair folds both masks into the
+            // count
+            static_assert(U % 2 == 0, "columns go in pairs");
+    #pragma unroll
+            for (int u = 0; u < U; u += 2) {
+                const int32_t xa = v[u], xb = v[u + 1];
+                const bool va = (uint32_t)xa < uE, vb = (uint32_t)xb < uE;
+                const int ia = va ? xa : E, ib = vb ? xb : E;  // padding and bad IDs rank in the sink cell
+                atomicOr(reinterpret_cast<unsigned long long *>(&cells[ia].mask), bit);
+                atomicOr(reinterpret_cast<unsigned long long *>(&cells[ib].mask1), bit);
+                wave_lds_fence();
+                const Cell ca = cells[ia];
+                const Cell cb = cells[ib];
+                const int32_t offa = STAGED && va ? offs[ia] : 0;
+                const int32_t offb = STAGED && vb ? offs[ib] : 0;
+                wave_lds_fence();
+                const uint64_t belowa = ca.mask & lt;
+                const uint64_t belowb = cb.mask1 & lt;
+                // one lane per expert of the pair: its lowest in the first column,
+                // else (absent there) its lowest in the second
+                if (belowa == 0)
+                    cells[ia] = make_cell<PAIR>(ca.kf + (uint32_t)__popcll(ca.mask) + (uint32_t)__popcll(ca.mask1), ca.base);
+                if (cb.mask == 0 && belowb == 0)
+                    cells[ib] = make_cell<PAIR>(cb.kf + (uint32_t)__popcll(cb.mask1), cb.base);
+                const int32_t ka = (int32_t)(ca.kf & kCountMask) + (int32_t)__popcll(belowa);
+                const int32_t kb = (int32_t)(cb.kf & kCountMask) + (int32_t)__popcll(cb.mask) + (int32_t)__popcll(belowb);
+                auto place = [&](const Cell &c, int xi, bool valid, int32_t off, int32_t k, int64_t i) {
+                    int32_t pos = (c.kf & (kNoneFlag | kSplitFlag)) ? -1 : c.base + k;
+                    if (c.kf & kSplitFlag) pos = position_of(inst, rfirst[xi], rcnt[xi], c.base + k);
+                    if (STAGED) stage[valid ? off + k : sub] = (uint16_t)(i - begin);
+                    else if (pos >= 0 && pos < N) src_out[pos] = (int32_t)i;
+                    if (i < end) __builtin_nontemporal_store(pos, pos_out + i);
+                };
+                place(ca, ia, va, offa, ka, g + u * kWave + lane);
+                place(cb, ib, vb, offb, kb, g + (u + 1) * kWave + lane);
+                wave_lds_fence();
+            }
+    
+        } else {
 #pragma unroll
-        for (int u = 0; u < U; u++) {
-            const int32_t x = v[u];
-            const bool valid = (uint32_t)x < uE;
-            const int xi = valid ? x : E;  // padding and bad IDs rank in the sink cell
-            atomicOr(reinterpret_cast<unsigned long long *>(&cells[xi].mask), bit);
-            wave_lds_fence();
-            const Cell cur = cells[xi];
-            const int32_t off = STAGED && valid ? offs[xi] : 0;
-            wave_lds_fence();
-            const int64_t i = g + u * kWave + lane;
-            const uint64_t below = cur.mask & lt;
-            if (below == 0) cells[xi] = Cell{0ull, cur.kf + (uint32_t)__popcll(cur.mask), cur.base};
-            const int32_t k = (int32_t)(cur.kf & kCountMask) + (int32_t)__popcll(below);
-            int32_t pos = (cur.kf & (kNoneFlag | kSplitFlag)) ? -1 : cur.base + k;
-            if (cur.kf & kSplitFlag) pos = position_of(inst, rfirst[xi], rcnt[xi], cur.base + k);
-            if (STAGED) stage[valid ? off + k : sub] = (uint16_t)(i - begin);
-            else if (pos >= 0 && pos < N) src_out[pos] = (int32_t)i;
-            if (i < end) __builtin_nontemporal_store(pos, pos_out + i);
-            wave_lds_fence();
+            for (int u = 0; u < U; u++) {
+                const int32_t x = v[u];
+                const bool valid = (uint32_t)x < uE;
+                const int xi = valid ? x : E;  // padding and bad IDs rank in the sink cell
+                atomicOr(reinterpret_cast<unsigned long long *>(&cells[xi].mask), bit);
+                wave_lds_fence();
+                const Cell cur = cells[xi];
+                const int32_t off = STAGED && valid ? offs[xi] : 0;
+                wave_lds_fence();
+                const int64_t i = g + u * kWave + lane;
+                const uint64_t below = cur.mask & lt;
+                if (below == 0) cells[xi] = make_cell<PAIR>(cur.kf + (uint32_t)__popcll(cur.mask), cur.base);
+                const int32_t k = (int32_t)(cur.kf & kCountMask) + (int32_t)__popcll(below);
+                int32_t pos = (cur.kf & (kNoneFlag | kSplitFlag)) ? -1 : cur.base + k;
+                if (cur.kf & kSplitFlag) pos = position_of(inst, rfirst[xi], rcnt[xi], cur.base + k);
+                if (STAGED) stage[valid ? off + k : sub] = (uint16_t)(i - begin);
+                else if (pos >= 0 && pos < N) src_out[pos] = (int32_t)i;
+                if (i < end) __builtin_nontemporal_store(pos, pos_out + i);
+                wave_lds_fence();
+            }
         }
     }
     if (STAGED) {
@@ -289,32 +352,35 @@ __global__ __launch_bounds__(W *kWave) void dispatch_kernel(
     }
 }
 
-int pick_dispatch_waves(int E, int Phi, int64_t stage) {
+int pick_dispatch_waves(int E, int Phi, int64_t stage, bool pair) {
     for (int w = 4; w >= 1; w >>= 1)
-        if (dispatch_lds_bytes(E, Phi, w, stage) <= 65536) return w;
+        if (dispatch_lds_bytes(E, Phi, w, stage, pair) <= 65536) return w;
     return 0;
 }
 
 }  // namespace
 
-size_t dispatch_lds_bytes(int E, int Phi, int waves, int64_t stage_pairs) {
+size_t dispatch_lds_bytes(int E, int Phi, int waves, int64_t stage_pairs, bool pair) {
     const size_t staged = stage_pairs > 0 ? (size_t)waves * ((size_t)stage_pairs / kWave * 8 + (size_t)E * 8 +
                                                              ((size_t)stage_pairs + kWave) * 2)
                                           : 0;
-    return (size_t)waves * (E + 1) * sizeof(Cell) + (size_t)Phi * 8 +
+    return (size_t)waves * (E + 1) * (pair ? sizeof(Cell2) : sizeof(Cell1)) + (size_t)Phi * 8 +
            (size_t)(Phi + 1) * 4 + (size_t)E * 8 + staged;
 }
 
-static const void *dispatch_fn(int w, bool staged) {
-    if (staged)
-        return w == 4 ? (const void *)dispatch_kernel<4, true>
-                      : w == 2 ? (const void *)dispatch_kernel<2, true> : (const void *)dispatch_kernel<1, true>;
-    return w == 4 ? (const void *)dispatch_kernel<4, false>
-                  : w == 2 ? (const void *)dispatch_kernel<2, false> : (const void *)dispatch_kernel<1, false>;
+template <bool ST, bool PR>
+static const void *dispatch_fn_w(int w) {
+    return w == 4 ? (const void *)dispatch_kernel<4, ST, PR>
+                  : w == 2 ? (const void *)dispatch_kernel<2, ST, PR> : (const void *)dispatch_kernel<1, ST, PR>;
 }
 
-static int resident_blocks(int w, bool staged, size_t lds) {
-    return ::ep::resident_blocks(dispatch_fn(w, staged), w * kWave, lds);
+static const void *dispatch_fn(int w, bool staged, bool pair) {
+    if (staged) return pair ? dispatch_fn_w<true, true>(w) : dispatch_fn_w<true, false>(w);
+    return pair ? dispatch_fn_w<false, true>(w) : dispatch_fn_w<false, false>(w);
+}
+
+static int resident_blocks(int w, bool staged, bool pair, size_t lds) {
+    return ::ep::resident_blocks(dispatch_fn(w, staged, pair), w * kWave, lds);
 }
 
 hipError_t launch_dispatch(const int32_t *ids, int64_t N, int32_t P, const ep_layout_t &L,
@@ -334,11 +400,16 @@ hipError_t launch_dispatch(const int32_t *ids, int64_t N, int32_t P, const ep_la
         (void)hipGetLastError();
         cus = 0;
     }
+    // Ranking two columns per LDS round trip pays where a few hot experts fill
+    // the columns (GLM-4.5-like and stress batches 25 % and 8 % faster), but its
+    // larger cells cost the 128-expert layout resident waves (17 % slower); so
+    // pairs above 128 experts, when their cells fit in LDS.
+    const bool pair = E > 128 && pick_dispatch_waves(E, Phi, 0, true) > 0;
     auto best_waves = [&](bool st, int &w_out) {
-        const int w0 = pick_dispatch_waves(E, Phi, st ? sub : 0);
+        const int w0 = pick_dispatch_waves(E, Phi, st ? sub : 0, pair);
         int best = w0, waves = -1;
         for (int c = w0; c >= 1; c >>= 1) {
-            const int r = resident_blocks(c, st, dispatch_lds_bytes(E, Phi, c, st ? sub : 0));
+            const int r = resident_blocks(c, st, pair, dispatch_lds_bytes(E, Phi, c, st ? sub : 0, pair));
             if (r * c > waves) { best = c; waves = r * c; }
         }
         w_out = w0 > 0 ? best : 0;
@@ -352,26 +423,31 @@ hipError_t launch_dispatch(const int32_t *ids, int64_t N, int32_t P, const ep_la
         if (wu > 0 && (!staged || wu_waves > ws_waves)) { staged = false; w = wu; }
     }
     if (w == 0) return hipErrorInvalidValue;
-    const size_t lds = dispatch_lds_bytes(E, Phi, w, staged ? sub : 0);
+    const size_t lds = dispatch_lds_bytes(E, Phi, w, staged ? sub : 0, pair);
     // Blocks per plan: every block builds the plan's route table once, so a
     // launch of many plans uses no more blocks than the GPU holds at once
     // (one round, equal work), each wave walking many sub-blocks.  At least one
     // block per plan, so the slot offsets are always written.
     int64_t nblk = nsb > 0 ? (nsb + w - 1) / w : 1;
-    const int resident = resident_blocks(w, staged, lds);
+    const int resident = resident_blocks(w, staged, pair, lds);
     if (resident > 0) {
         const int64_t per_plan = resident / P > 0 ? resident / P : 1;
         if (per_plan < nblk) nblk = per_plan;
     }
     dim3 grid((unsigned)nblk, (unsigned)P);
-#define EP_DISPATCH(WV, ST)                                                                        \
-    hipLaunchKernelGGL((dispatch_kernel<WV, ST>), grid, dim3(WV * kWave), lds, s, ids, N, E, Phi, rho, \
+#define EP_DISPATCH(WV, ST, PR)                                                                         \
+    hipLaunchKernelGGL((dispatch_kernel<WV, ST, PR>), grid, dim3(WV * kWave), lds, s, ids, N, E, Phi, rho, \
                        sub, nsb, sps, nseg, ws, phy_quota, log2phy, logcnt, slot_offsets, dpos, dsrc)
+#define EP_DISPATCH_W(ST, PR)                                                                           \
+    do {                                                                                                \
+        if (w == 4) EP_DISPATCH(4, ST, PR); else if (w == 2) EP_DISPATCH(2, ST, PR); else EP_DISPATCH(1, ST, PR); \
+    } while (0)
     if (staged) {
-        if (w == 4) EP_DISPATCH(4, true); else if (w == 2) EP_DISPATCH(2, true); else EP_DISPATCH(1, true);
+        if (pair) EP_DISPATCH_W(true, true); else EP_DISPATCH_W(true, false);
     } else {
-        if (w == 4) EP_DISPATCH(4, false); else if (w == 2) EP_DISPATCH(2, false); else EP_DISPATCH(1, false);
+        if (pair) EP_DISPATCH_W(false, true); else EP_DISPATCH_W(false, false);
     }
+#undef EP_DISPATCH_W
 #undef EP_DISPATCH
     return hipGetLastError();
 }

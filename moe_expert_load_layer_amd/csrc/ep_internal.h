@@ -336,7 +336,7 @@ hipError_t launch_dispatch(const int32_t *ids, int64_t N, int32_t P, const ep_la
                            const SubGeom &g, const int32_t *ws, const int32_t *phy_quota,
                            const int32_t *log2phy, const int32_t *logcnt, int32_t *slot_offsets,
                            int32_t *dpos, int32_t *dsrc, hipStream_t s);
-size_t dispatch_lds_bytes(int E, int Phi, int waves, int64_t stage_pairs);
+size_t dispatch_lds_bytes(int E, int Phi, int waves, int64_t stage_pairs, bool pair);
 hipError_t launch_grad_reduce(float *native, int64_t n, const float *slot, const int32_t *log2phy,
                               const int32_t *logcnt, const ep_layout_t &L, hipStream_t s);
 hipError_t launch_slot_fill(const void *w, int64_t bytes_per_expert, const int32_t *phy2log,
