@@ -156,19 +156,40 @@ def test_plan_max_replicas_64(dev):
     _assert_plan_equal(out, refs)
 
 
-def test_plan_step_cap_flag(dev):
-    # rank 0 hosts all 6 hot experts; rank 1..3 have 3 spares each: the cap is
-    # 2*S+R = 22 moves; check the flag agrees with the oracle whatever it is
-    E, nc, ne, sc = 6, [6, 0, 0, 0], list(range(6)), [0, 3, 3, 3]
-    lay_o = oracle.Layout.of(E, 4, nc, ne, sc)
-    loads = np.array([[1000, 999, 998, 997, 996, 995]], np.int32)
-    ref = oracle.plan(loads[0], lay_o)
+# The hand-traced run that reaches the move cap (2*S + R = 9 moves), pinned on
+# the CPU in tests/test_oracle_plan.py: rank 1 takes replicas of experts 0 and 2
+# in its spare slots 3 and 4 (lowest free slot first), and the flag is set.  The
+# first layout (one native per rank) runs the rank-per-lane planner; the second
+# adds eight idle natives to rank 2, more than the lane planner's eight per rank,
+# so the generic LDS planner runs the same moves.
+_CAP_CASES = {
+    "lanes": (3, [1, 1, 1], list(range(3)), [1, 2, 0], [37, 6, 34]),
+    "generic": (11, [1, 1, 9], list(range(11)), [1, 2, 0], [37, 6, 34] + [0] * 8),
+}
+
+
+@pytest.mark.parametrize("kernel", sorted(_CAP_CASES))
+def test_plan_step_cap_binds(dev, kernel):
+    E, nc, ne, sc, hot = _CAP_CASES[kernel]
+    assert (max(nc) > 8) == (kernel == "generic")
+    lay_o = oracle.Layout.of(E, 3, nc, ne, sc)
+    # plan 0: the cap case; plan 1: the same loads halved (checked against the
+    # oracle, whatever it does); plan 2: no load at all
+    loads = np.array([hot, [v // 2 for v in hot], [0] * E], np.int32)
+    refs = [oracle.plan(l, lay_o) for l in loads]
+    assert (refs[0].steps, refs[0].cap_hit) == (9, 1)
+    assert refs[0].phy2log.tolist()[:6] == [0, -1, 1, 0, 2, 2]
+    assert refs[0].phy_quota.tolist()[:6] == [25, 0, 6, 12, 8, 26]
+    print(f"[plan cap] {kernel} E={E}", flush=True)
     lay = ep.Layout.create(E, nc, ne, sc, device=dev)
-    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    status = torch.full((3,), 0x40, dtype=torch.int32, device=dev)
     out = ep.ep_plan_quota(torch.from_numpy(loads).to(dev), lay, status=status)
     torch.cuda.synchronize()
-    _assert_plan_equal(out, [ref])
-    assert int(status[0]) == (ep.EP_STATUS_STEP_CAP if ref.cap_hit else 0)
+    _assert_plan_equal(out, refs)
+    st = _np(status)
+    for p, r in enumerate(refs):
+        # the planner ORs its flag into the caller's word and leaves other bits
+        assert int(st[p]) == 0x40 | (ep.EP_STATUS_STEP_CAP if r.cap_hit else 0)
 
 
 # --------------------------------------------------------------------- A3

@@ -154,6 +154,56 @@ def test_plan_by_hand_ties():
     assert (pl.steps, pl.cap_hit) == (4, 0)
 
 
+def test_plan_by_hand_step_cap_and_spare_order():
+    # ranks 0,1,2 host experts 0,1,2; spares (1, 2, 0); loads (37, 6, 34).
+    # slots: r0 = {0: e0, 1: spare}, r1 = {2: e1, 3: spare, 4: spare}, r2 = {5: e2}
+    # cap = 2*S + R = 2*3 + 3 = 9 moves.
+    # step 1: h=0 (37).  e0 has one instance; replicate: ranks with a free spare and
+    #         no e0 = {1} -> rank 1, its LOWEST free spare = slot 3.  Water-fill 37
+    #         over backgrounds (0 on r0, 6 on r1): level 43/2 -> 22 and 15.
+    #         loads (22, 21, 34)
+    # step 2: h=2.  Replicate e2: ranks {0: 22, 1: 21} -> rank 1, next free spare =
+    #         slot 4.  Water-fill 34 over (0 on r2, 21 on r1): 55/2 -> 28 and 6.
+    #         loads (22, 27, 28)
+    # step 3: h=2.  Re-level e2 gives 28 again; replicate e2 onto rank 0 (rank 1 is
+    #         full), slot 1: 34 over (0 on r2, 21 on r1, 22 on r0): 77/3 = 25 rem 2
+    #         -> 26, 5, 3.  loads (25, 26, 26); every spare is now taken.
+    # step 4: h=1 (tie with r2).  Candidates e0 (15), e1 (6), e2 (5).  Re-level e0
+    #         over (3 on r0, 11 on r1): 51/2 -> 23 and 14.  loads (26, 25, 26)
+    # step 5: h=0.  Re-level e0 gives 23 again; e2 over (0 on r2, 20 on r1, 23 on
+    #         r0): 77/3 -> 26, 6, 2.  loads (25, 26, 26)
+    # step 6: h=1.  e0 over (2 on r0, 12 on r1) -> 24 and 13.  loads (26, 25, 26)
+    # step 7: h=0.  e2 over (0, 19 on r1, 24 on r0) -> 26, 7, 1.  loads (25, 26, 26)
+    # step 8: h=1.  e0 over (1 on r0, 13 on r1) -> 25 and 12.  loads (26, 25, 26)
+    # step 9: h=0.  e2 over (0, 18 on r1, 25 on r0) -> 26, 8, 0.  loads (25, 26, 26)
+    # 9 moves = the cap: the loop stops with the flag set (a tenth move, re-levelling
+    # e0 on rank 1, would still lower the hottest rank).  The replica of e2 on rank 0
+    # ends with quota 0 and is freed.
+    lay = oracle.Layout.of(3, 3, [1, 1, 1], [0, 1, 2], [1, 2, 0])
+    pl = oracle.plan(np.array([37, 6, 34]), lay)
+    assert pl.phy2log.tolist() == [0, -1, 1, 0, 2, 2]
+    assert pl.phy_quota.tolist() == [25, 0, 6, 12, 8, 26]
+    assert pl.logcnt.tolist() == [2, 1, 2]
+    assert pl.log2phy.tolist() == [[0, 3, -1], [2, -1, -1], [4, 5, -1]]
+    assert (pl.steps, pl.cap_hit) == (9, 1)
+
+
+def test_plan_by_hand_step_cap_with_idle_natives():
+    # The same run with eight more experts (3..10) native on rank 2 and never
+    # loaded: they are no candidates and change no background, so every move and
+    # the cap (2*3 + 3 = 9) are as above; only rank 2's slots are renumbered
+    # (5: e2, 6..13: e3..e10).
+    lay = oracle.Layout.of(11, 3, [1, 1, 9], list(range(11)), [1, 2, 0])
+    load = np.zeros(11, np.int64)
+    load[:3] = [37, 6, 34]
+    pl = oracle.plan(load, lay)
+    assert pl.phy2log.tolist() == [0, -1, 1, 0, 2, 2] + list(range(3, 11))
+    assert pl.phy_quota.tolist() == [25, 0, 6, 12, 8, 26] + [0] * 8
+    assert pl.logcnt.tolist() == [2, 1, 2] + [1] * 8
+    assert pl.log2phy.tolist()[:3] == [[0, 3, -1], [2, -1, -1], [4, 5, -1]]
+    assert (pl.steps, pl.cap_hit) == (9, 1)
+
+
 # ------------------------------------------------------------ invariants
 def check_plan_invariants(load, lay, pl):
     E, Phi = lay.num_experts, lay.num_phys
