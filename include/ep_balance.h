@@ -23,6 +23,7 @@
  *
  * All EP ranks of one layer are simulated on one GPU: the rank is an array
  * axis.  One "plan" is one (microbatch, layer); calls take P plans at once.
+
  *
  * Conventions shared by every call
  *   - Pointers named as device data are device pointers owned by the caller;
@@ -54,6 +55,7 @@ enum {
     EP_OK = 0,
     EP_ERR_INVALID_ARG = -1,
     EP_ERR_HIP = -2,
+    EP_ERR_TOO_LARGE = -3, /* ep_route_noalloc: the batch needs more than its scratch */
 };
 
 /* bits of the per-plan status word */
@@ -122,6 +124,7 @@ int ep_layout_init(int32_t num_experts, int32_t num_ranks, const int32_t *native
  * pair, plus about 1 byte per pair with E <= 256.
  */
 size_t ep_workspace_bytes(int64_t pairs_per_plan, int32_t num_plans, int32_t num_experts);
+
 
 /*
  * A1 -- exact per-expert load of every plan (UltraEP article, key designs:
@@ -274,6 +277,33 @@ int ep_replica_grad_reduce(float *native_grads, int64_t elems_per_expert, const 
 int ep_balance_stats(const int32_t *load, const int32_t *phy_quota, int32_t num_plans,
                      const ep_layout_t *layout, int64_t *stats, double *imbalance,
                      int32_t *rank_load, ep_stream_t stream);
+
+/*
+ * For callers that cannot allocate device memory (code under graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): ep_load_histogram,
+ * ep_plan_quota and ep_reroute in one call, with the workspace that carries
+ * the histogram's per-sub-block counts (and byte copy) to the reroute held in
+ * a device array of the library instead of a caller buffer.  The outputs are
+ * exactly those of the three calls (same arguments, same meaning, same
+ * layouts; status is written as the histogram writes it, then the planner's
+ * flag is OR-ed in).  The call allocates nothing and never synchronises.
+ *
+ * The array is EP_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU, held by every GPU
+ * the library runs this call on until the process ends.  A batch whose
+ * workspace, ep_workspace_bytes(N, P, E), is larger returns EP_ERR_TOO_LARGE
+ * and enqueues nothing; 64 MiB holds, for example, 14 plans of 4.2M pairs at
+ * E = 128 (a plan = one layer of an EP64 group with 8192 tokens per rank,
+ * top-8) or 75 such plans at E = 384.  All argument checks of the three calls run before
+ * anything is enqueued.  Every call on one GPU shares that GPU's array, so
+ * calls whose work overlaps on one GPU (other streams, other host threads)
+ * race and corrupt each other's results: serialise them (one stream, or
+ * events) on each GPU.
+ */
+#define EP_NOALLOC_SCRATCH_BYTES (64u << 20)
+int ep_route_noalloc(const int32_t *topk_ids, int64_t pairs_per_plan, int32_t num_plans,
+                     const ep_layout_t *layout, int32_t *load, uint32_t *status, int32_t *phy2log,
+                     int32_t *phy_quota, int32_t *logcnt, int32_t *log2phy, int32_t *steps,
+                     int32_t *phys_ids, ep_stream_t stream);
 
 /* Human-readable name of a return code. */
 const char *ep_status_string(int code);

@@ -21,6 +21,8 @@ LIB_PATH = os.path.join(HERE, "libepbalance.so")
 EP_OK = 0
 EP_ERR_INVALID_ARG = -1
 EP_ERR_HIP = -2
+EP_ERR_TOO_LARGE = -3
+EP_NOALLOC_SCRATCH_BYTES = 64 << 20
 EP_STATUS_BAD_ID = 1
 EP_STATUS_STEP_CAP = 2
 
@@ -67,10 +69,12 @@ def lib() -> ctypes.CDLL:
         L.ep_dispatch_layout.argtypes = [vp, i64, i32, lp, vp, vp, vp, vp, sz, vp, vp, vp, vp]
         L.ep_replica_grad_reduce.argtypes = [vp, i64, vp, vp, vp, lp, vp]
         L.ep_balance_stats.argtypes = [vp, vp, i32, lp, vp, vp, vp, vp]
+        L.ep_route_noalloc.argtypes = [vp, i64, i32, lp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.ep_status_string.argtypes = [ctypes.c_int]
         L.ep_status_string.restype = ctypes.c_char_p
         for f in ("ep_layout_init", "ep_load_histogram", "ep_plan_quota", "ep_reroute",
-                  "ep_slot_fill", "ep_balance_stats", "ep_dispatch_layout", "ep_replica_grad_reduce"):
+                  "ep_slot_fill", "ep_balance_stats", "ep_dispatch_layout", "ep_replica_grad_reduce",
+                  "ep_route_noalloc"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -290,6 +294,24 @@ def ep_replica_grad_reduce(native_grads: torch.Tensor, slot_grads: torch.Tensor,
                                       _ptr(log2phy), _ptr(logcnt), layout.ref(), _stream(stream))
     _check(rc, "ep_replica_grad_reduce")
     return native_grads
+
+
+def ep_route_noalloc(topk_ids: torch.Tensor, layout: Layout, load: torch.Tensor, status: torch.Tensor,
+                     plan: PlanOut, phys_ids: torch.Tensor, stream=None):
+    """hist -> plan -> reroute in one call that allocates nothing: the workspace is
+    the library's own device array (EP_NOALLOC_SCRATCH_BYTES per GPU).  Every
+    output is the caller's; calls that overlap on one GPU race."""
+    P, N = _ids(topk_ids)
+    _arg(load, torch.int32, (P, layout.num_experts), "load"); _arg(status, torch.int32, (P,), "status")
+    _arg(plan.phy2log, torch.int32, (P, layout.num_phys), "phy2log")
+    _plan_args(layout, P, plan.phy_quota, plan.log2phy, plan.logcnt)
+    _arg(plan.steps, torch.int32, (P,), "steps")
+    _arg(phys_ids, torch.int32, (P, N), "phys_ids")
+    rc = lib().ep_route_noalloc(_ptr(topk_ids), N, P, layout.ref(), _ptr(load), _ptr(status),
+                                _ptr(plan.phy2log), _ptr(plan.phy_quota), _ptr(plan.logcnt),
+                                _ptr(plan.log2phy), _ptr(plan.steps), _ptr(phys_ids), _stream(stream))
+    _check(rc, "ep_route_noalloc")
+    return load, status, plan, phys_ids
 
 
 def ep_slot_fill(expert_weights: torch.Tensor, phy2log: torch.Tensor, layout: Layout,

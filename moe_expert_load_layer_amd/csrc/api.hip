@@ -42,6 +42,42 @@ bool pairs_ok(const int32_t *ids, int64_t N, int32_t P) {
 
 }  // namespace
 
+namespace ep {
+
+int check_histogram(const int32_t *topk_ids, int64_t N, int32_t P, const ep_layout_t *layout,
+                    const int32_t *load, const void *ws, size_t ws_size, const uint32_t *status) {
+    if (!layout_ok(layout) || !pairs_ok(topk_ids, N, P) || !load || !status) return EP_ERR_INVALID_ARG;
+    const int E = layout->num_experts;
+    if ((size_t)kSegSubs * (E + 1) * 4 > kMaxLds) return EP_ERR_INVALID_ARG;
+    const size_t need = ws_bytes(N, P, E);
+    if (ws_size < need || (need > 0 && (!ws || !aligned(ws, 16)))) return EP_ERR_INVALID_ARG;
+    return EP_OK;
+}
+
+int check_plan(const int32_t *load, int32_t P, const ep_layout_t *layout, const int32_t *phy2log,
+               const int32_t *phy_quota, const int32_t *logcnt, const int32_t *log2phy) {
+    if (!layout_ok(layout) || !load || !phy2log || !phy_quota || !logcnt || !log2phy)
+        return EP_ERR_INVALID_ARG;
+    if (P < 1 || P > kMaxPlans || layout->max_replicas > 64) return EP_ERR_INVALID_ARG;
+    if (plan_lanes_cfg(*layout) == 0 && plan_lds_bytes(*layout) > kMaxLds) return EP_ERR_INVALID_ARG;
+    return EP_OK;
+}
+
+int check_reroute(const int32_t *topk_ids, int64_t N, int32_t P, const ep_layout_t *layout,
+                  const int32_t *phy_quota, const int32_t *log2phy, const int32_t *logcnt, const void *ws,
+                  size_t ws_size, const int32_t *phys_ids) {
+    if (!layout_ok(layout) || !pairs_ok(topk_ids, N, P) || !phy_quota || !log2phy || !logcnt)
+        return EP_ERR_INVALID_ARG;
+    if (N > 0 && (!phys_ids || !aligned(phys_ids, 4))) return EP_ERR_INVALID_ARG;
+    const int E = layout->num_experts;
+    if (reroute_lds_bytes(E, layout->num_phys, 1) > kMaxLds) return EP_ERR_INVALID_ARG;
+    const size_t need = ws_bytes(N, P, E);
+    if (ws_size < need || (need > 0 && (!ws || !aligned(ws, 16)))) return EP_ERR_INVALID_ARG;
+    return EP_OK;
+}
+
+}  // namespace ep
+
 extern "C" {
 
 size_t ep_layout_table_ints(int32_t num_experts, int32_t num_ranks, int32_t num_spare) {
@@ -126,11 +162,9 @@ size_t ep_workspace_bytes(int64_t pairs_per_plan, int32_t num_plans, int32_t num
 int ep_load_histogram(const int32_t *topk_ids, int64_t N, int32_t P, const ep_layout_t *layout,
                       int32_t *load, void *ws, size_t ws_size, uint32_t *status,
                       ep_stream_t stream) {
-    if (!layout_ok(layout) || !pairs_ok(topk_ids, N, P) || !load || !status) return EP_ERR_INVALID_ARG;
+    const int rc = check_histogram(topk_ids, N, P, layout, load, ws, ws_size, status);
+    if (rc != EP_OK) return rc;
     const int E = layout->num_experts;
-    if ((size_t)kSegSubs * (E + 1) * 4 > kMaxLds) return EP_ERR_INVALID_ARG;
-    const size_t need = ws_bytes(N, P, E);
-    if (ws_size < need || (need > 0 && (!ws || !aligned(ws, 16)))) return EP_ERR_INVALID_ARG;
     return hip_rc(launch_histogram(topk_ids, N, P, E, sub_geom(N, P, E), static_cast<int32_t *>(ws),
                                    compact_of(ws, N, P, E), load, status, as_stream(stream)));
 }
@@ -138,11 +172,9 @@ int ep_load_histogram(const int32_t *topk_ids, int64_t N, int32_t P, const ep_la
 int ep_plan_quota(const int32_t *load, int32_t P, const ep_layout_t *layout, int32_t *phy2log,
                   int32_t *phy_quota, int32_t *logcnt, int32_t *log2phy, int32_t *steps,
                   uint32_t *status, ep_stream_t stream) {
-    if (!layout_ok(layout) || !load || !phy2log || !phy_quota || !logcnt || !log2phy)
-        return EP_ERR_INVALID_ARG;
-    if (P < 1 || P > kMaxPlans || layout->max_replicas > 64) return EP_ERR_INVALID_ARG;
+    const int rc = check_plan(load, P, layout, phy2log, phy_quota, logcnt, log2phy);
+    if (rc != EP_OK) return rc;
     const int cfg = plan_lanes_cfg(*layout);
-    if (cfg == 0 && plan_lds_bytes(*layout) > kMaxLds) return EP_ERR_INVALID_ARG;
     return hip_rc(launch_plan(load, P, *layout, phy2log, phy_quota, logcnt, log2phy, steps, status,
                               as_stream(stream), cfg));
 }
@@ -150,13 +182,9 @@ int ep_plan_quota(const int32_t *load, int32_t P, const ep_layout_t *layout, int
 int ep_reroute(const int32_t *topk_ids, int64_t N, int32_t P, const ep_layout_t *layout,
                const int32_t *phy_quota, const int32_t *log2phy, const int32_t *logcnt,
                const void *ws, size_t ws_size, int32_t *phys_ids, ep_stream_t stream) {
-    if (!layout_ok(layout) || !pairs_ok(topk_ids, N, P) || !phy_quota || !log2phy || !logcnt)
-        return EP_ERR_INVALID_ARG;
-    if (N > 0 && (!phys_ids || !aligned(phys_ids, 4))) return EP_ERR_INVALID_ARG;
+    const int rc = check_reroute(topk_ids, N, P, layout, phy_quota, log2phy, logcnt, ws, ws_size, phys_ids);
+    if (rc != EP_OK) return rc;
     const int E = layout->num_experts;
-    if (reroute_lds_bytes(E, layout->num_phys, 1) > kMaxLds) return EP_ERR_INVALID_ARG;
-    const size_t need = ws_bytes(N, P, E);
-    if (ws_size < need || (need > 0 && (!ws || !aligned(ws, 16)))) return EP_ERR_INVALID_ARG;
     return hip_rc(launch_reroute(topk_ids, N, P, *layout, sub_geom(N, P, E), static_cast<const int32_t *>(ws),
                                  compact_of(const_cast<void *>(ws), N, P, E), phy_quota, log2phy,
                                  logcnt, phys_ids, as_stream(stream)));
@@ -218,6 +246,7 @@ const char *ep_status_string(int code) {
         case EP_OK: return "EP_OK";
         case EP_ERR_INVALID_ARG: return "EP_ERR_INVALID_ARG";
         case EP_ERR_HIP: return "EP_ERR_HIP";
+        case EP_ERR_TOO_LARGE: return "EP_ERR_TOO_LARGE";
         default: return "EP_UNKNOWN";
     }
 }

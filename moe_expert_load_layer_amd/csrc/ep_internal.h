@@ -317,6 +317,17 @@ int resident_blocks(const void *fn, int threads, size_t lds);
 // ---------------------------------------------------------------------------
 // launchers (defined in the .hip files; return hipError_t of the launch)
 // ---------------------------------------------------------------------------
+// Host-side argument checks of ep_load_histogram, ep_plan_quota and
+// ep_reroute (EP_OK or the error code the call returns); the no-allocation
+// chain runs all three before it enqueues anything.
+int check_histogram(const int32_t *topk_ids, int64_t N, int32_t P, const ep_layout_t *layout,
+                    const int32_t *load, const void *ws, size_t ws_size, const uint32_t *status);
+int check_plan(const int32_t *load, int32_t P, const ep_layout_t *layout, const int32_t *phy2log,
+               const int32_t *phy_quota, const int32_t *logcnt, const int32_t *log2phy);
+int check_reroute(const int32_t *topk_ids, int64_t N, int32_t P, const ep_layout_t *layout,
+                  const int32_t *phy_quota, const int32_t *log2phy, const int32_t *logcnt, const void *ws,
+                  size_t ws_size, const int32_t *phys_ids);
+
 hipError_t launch_histogram(const int32_t *ids, int64_t N, int32_t P, int32_t E, const SubGeom &g,
                             int32_t *ws, const Compact &cp, int32_t *load, uint32_t *status,
                             hipStream_t s);

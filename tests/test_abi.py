@@ -21,7 +21,7 @@ def test_header_declares_the_path():
     names = _declared()
     for n in ("ep_load_histogram", "ep_plan_quota", "ep_reroute", "ep_slot_fill", "ep_balance_stats",
               "ep_workspace_bytes", "ep_layout_init", "ep_layout_table_ints", "ep_status_string",
-              "ep_dispatch_layout", "ep_replica_grad_reduce"):
+              "ep_dispatch_layout", "ep_replica_grad_reduce", "ep_route_noalloc"):
         assert n in names
 
 
@@ -41,6 +41,7 @@ def test_host_side_checks_without_gpu():
     L = ep.lib()
     assert L.ep_status_string(0) == b"EP_OK"
     assert L.ep_status_string(-1) == b"EP_ERR_INVALID_ARG"
+    assert L.ep_status_string(-3) == b"EP_ERR_TOO_LARGE"
     assert L.ep_layout_table_ints(12, 8, 4) == 2 * 8 + 1 + 3 * 16 + 12 + 4
     assert L.ep_workspace_bytes(-1, 1, 4) == 0
     assert L.ep_workspace_bytes(0, 3, 4) == 3 * 1 * 5 * 4      # only the per-plan totals row
@@ -135,3 +136,21 @@ def test_bench_sub_block_rule_matches_the_library():
         rows = P * (nsb + nseg + 1) * (E + 1) * 4
         want = a(rows) + a(P * nsb * 4) + P * ((N + 15) // 16 * 16) if E <= 256 else rows
         assert ep.ep_workspace_bytes(N, P, E) == want, (N, P, E)
+
+
+def test_noalloc_host_checks_without_gpu():
+    # a batch whose workspace exceeds the library's scratch is refused on the
+    # host (before any HIP call), and so is a missing layout
+    import moe_expert_load_layer_amd as ep
+    if not os.path.exists(ep.LIB_PATH):
+        pytest.skip("library not built")
+    L = ep.lib()
+    lay = ep._CLayout(128, 64, 192, 64, 64, 2, 1, 0, None)
+    N, P = 64 * 8192 * 8, 16
+    assert L.ep_workspace_bytes(N, P, 128) > ep.EP_NOALLOC_SCRATCH_BYTES
+    nul = [None] * 8
+    assert L.ep_route_noalloc(None, N, P, ctypes.byref(lay), *nul, None) == ep.EP_ERR_TOO_LARGE
+    assert L.ep_route_noalloc(None, N, 1, None, *nul, None) == ep.EP_ERR_INVALID_ARG
+    assert L.ep_route_noalloc(None, -1, 1, ctypes.byref(lay), *nul, None) == ep.EP_ERR_INVALID_ARG
+    assert L.ep_route_noalloc(None, N, 70000, ctypes.byref(lay), *nul, None) == ep.EP_ERR_INVALID_ARG
+
