@@ -1,9 +1,11 @@
 """Full-size parity: every workload at its full size, all plans in one launch
 (the launch configuration bench.py times), against the CPU oracle.
 
-Histogram, plan, reroute and statistics are compared in full; the slot fill
-(gigabytes per layer) is compared on sampled 16-byte-aligned windows of every
-used spare slot, and empty slots must keep their sentinel bytes.
+Histogram, plan, reroute and statistics are compared in full.  The slot fill
+(gigabytes per layer) is compared byte for byte on the device: every used spare
+slot's row must equal the weights row of the expert the oracle's plan puts
+there, and every empty slot's row must keep its sentinel bytes; sampled windows
+are also brought to the host and compared there.
 """
 import numpy as np
 import pytest
@@ -77,11 +79,13 @@ def test_fullsize_single_layer(dev, name):
     torch.cuda.synchronize()
     ids_h = ids.cpu().numpy()[0]
     lay_o = oracle.Layout.from_workload(wl)
-    ld, _ = oracle.histogram(ids_h, E)
+    ld, bad = oracle.histogram(ids_h, E)
     assert np.array_equal(out["load"][0].cpu().numpy(), ld)
     pl = oracle.plan(ld, lay_o)
-    assert np.array_equal(pl_g.phy_quota[0].cpu().numpy(), pl.phy_quota)
-    assert np.array_equal(pl_g.log2phy[0].cpu().numpy(), pl.log2phy)
+    for k in ("phy2log", "phy_quota", "logcnt", "log2phy"):
+        assert np.array_equal(getattr(pl_g, k)[0].cpu().numpy(), getattr(pl, k)), k
+    assert int(pl_g.steps[0]) == pl.steps
+    assert int(out["status"][0]) == (ep.EP_STATUS_STEP_CAP if pl.cap_hit else 0) | (ep.EP_STATUS_BAD_ID if bad else 0)
     ph, _ = oracle.reroute(ids_h, E, pl.phy_quota, pl.log2phy, pl.logcnt)
     assert np.array_equal(out["phys"][0].cpu().numpy(), ph)
     ro, rp, rs, _ = oracle.dispatch(ids_h, E, pl.phy_quota, pl.log2phy, pl.logcnt)
@@ -113,6 +117,13 @@ def test_fullsize_slot_fill(dev, name):
         s16.fill_(0x7FC1)
         ep.ep_slot_fill(weights, torch.from_numpy(pl.phy2log).to(dev), lay, slot)
         torch.cuda.synchronize()
+        # every byte, on the device
+        for o, s in enumerate(spare):
+            e = int(pl.phy2log[s])
+            if e >= 0:
+                assert torch.equal(s16[o], w16[e]), f"plan {p} slot {o} expert {e}"
+            else:
+                assert bool((s16[o] == 0x7FC1).all()), f"plan {p} empty slot {o} was written"
         for o, s in enumerate(spare):
             e = int(pl.phy2log[s])
             starts = list(rng.integers(0, max(1, elems - win), size=6) // 8 * 8) + [0, max(0, elems - win)]

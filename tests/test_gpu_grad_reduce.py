@@ -64,7 +64,9 @@ def test_grad_reduce_order_by_hand(dev):
 
 def test_grad_reduce_fullsize_sampled(dev):
     # Qwen3-235B-like layer: 3x4096x1536 fp32 gradient per expert; every element
-    # is independent, so sampled windows of every row are folded by the oracle
+    # is independent, so sampled windows of every row are folded by the oracle,
+    # and every element of every row is compared on the device with the fold
+    # written out in slot order (first instance, then + each next instance)
     wl = W.get("qwen3_235b")
     lay_o = oracle.Layout.from_workload(wl)
     pl = _plan(wl, lay_o, tokens=wl.tokens_per_rank)
@@ -78,9 +80,33 @@ def test_grad_reduce_fullsize_sampled(dev):
     w = 1024
     before_n = [d_native[:, a:a + w].cpu().numpy() for a in starts]
     before_s = [d_slot[:, a:a + w].cpu().numpy() for a in starts]
+    # the expected rows of the replicated experts, built before the call
+    _, home, _, spare = lay_o.slots()
+    ordinal = {int(s): o for o, s in enumerate(spare)}
+    expect = {}
+    for e in range(wl.num_experts):
+        c = int(pl.logcnt[e])
+        if c < 2:
+            continue
+        rows = [d_native[int(home[s])] if home[s] >= 0 else d_slot[ordinal[int(s)]]
+                for s in pl.log2phy[e, :c]]
+        acc = rows[0].clone()
+        for r in rows[1:]:
+            acc = acc + r
+        expect[e] = acc
+    untouched = [e for e in range(wl.num_experts) if e not in expect][:4]
+    keep = {e: d_native[e].clone() for e in untouched}
+    slot_before = d_slot.clone()
     ep.ep_replica_grad_reduce(d_native, d_slot, torch.from_numpy(pl.log2phy).to(dev),
                               torch.from_numpy(pl.logcnt).to(dev), lay)
     torch.cuda.synchronize()
+    assert len(expect) > 10
+    for e, acc in expect.items():
+        assert torch.equal(d_native[e].view(torch.int32), acc.view(torch.int32)), f"expert {e}"
+    for e, row in keep.items():
+        assert torch.equal(d_native[e], row), f"expert {e} (one instance) changed"
+    assert torch.equal(d_slot, slot_before)
+    del expect, keep, slot_before
     for a, bn, bs in zip(starts, before_n, before_s):
         ref = np.ascontiguousarray(bn)
         oracle.grad_reduce(ref, np.ascontiguousarray(bs), lay_o, pl.log2phy, pl.logcnt)
