@@ -13,12 +13,27 @@ Inputs are synthetic, seeded, and resident in HBM before timing starts.
 
 value = (token,k) pairs per second through hist + plan + reroute (HIP events
 around that phase in every timed step); ms_per_step is the whole step
-including the slot fills and statistics.  The roofline object covers the
-dominant kernel (slot fill): algorithmic bytes = (distinct experts among the
-filled spare slots + filled slots) * bytes_per_expert (each replicated expert
-read once, each slot written once), divided by the mean launch time from HIP
-events on the stream the kernel runs on.  The CPU baseline times the C oracle
-on a bounded sample of the same layers on the host.
+including the slot fills and statistics.
+
+Byte rules (algorithmic bytes per unit of work):
+  path        12 B per pair: the ID read by the histogram (4), read again and the
+              physical slot written by the reroute (4 + 4)
+  histogram   4 B per pair; reroute 8 B per pair (the same split)
+  slot fill   2 x bytes_per_expert per filled spare slot (each slot's expert
+              read and the slot written)
+Beside each, the bytes the kernels actually move: with E <= 256 the histogram
+writes a one-byte copy of each ID that the reroute reads instead (5 + 5 B per
+pair with the count rows), and the slot fill reads each distinct expert once for
+all the slots that hold it ((distinct experts + filled slots) x bytes_per_expert).
+
+The roofline object covers the dominant kernel, the slot fill: `achieved` and
+`frac` on the first rule, `achieved_moved` and `frac_moved` on the bytes moved,
+from the mean launch time measured with HIP events on the stream the fills run
+on.  `traffic` is the HBM bytes per launch from the rocprofv3 FETCH_SIZE and
+WRITE_SIZE summary committed for this kernel source (null when the source has
+changed since).  The `workloads` object repeats the measurement, compactly, for
+every workload.  The CPU baseline times the C oracle on a bounded sample of the
+same layers on the host (hist + plan + reroute, and the slot fill as memcpy).
 """
 from __future__ import annotations
 
@@ -42,25 +57,34 @@ import workloads as W  # noqa: E402
 HBM_PEAK_GBPS = 8000.0
 METRIC = "(token,k) pairs/s via hist+plan+reroute; plan µs/layer at EP64; HBM GB/s"
 
-# HBM bytes per slot-fill launch measured with rocprofv3 --pmc (FETCH_SIZE and
-# WRITE_SIZE), scaled by the same counters on a plain copy of known size; valid
-# only for the kernel source they were taken on.
-TRAFFIC = {"kernel_sha": "98e1c4c10e601569", "fetch_kib": 483585.7, "write_kib": 2290701.0, "fetch_scale": 2.0, "write_scale": 1.0, "bytes_per_launch": 3336061381}
+PATH_BYTES_PER_PAIR = 12.0      # hist 4 (ID in) + reroute 8 (ID in, slot out)
+HIST_BYTES_PER_PAIR = 4.0
+REROUTE_BYTES_PER_PAIR = 8.0
+FILL_RULE = "2 x bytes_per_expert per filled spare slot (read + write per slot)"
+FILL_MOVED_RULE = "(distinct experts in filled spare slots + filled slots) x bytes_per_expert"
 
 
-def _sub_pairs(N: int, P: int, E: int) -> int:
-    """The library's sub-block size for P plans of N pairs: about 8192 waves per
-    launch, a power of two from 1024 to 4096 pairs, and at least 8 (E + 1) pairs
-    (16 (E + 1) above 256 experts)."""
-    want = -(-N * P // 8192)
-    lo = max(1024, (8 if E <= 256 else 16) * (E + 1))
-    want = max(want, lo)
-    sub = 1024
-    while sub < want and sub < 4096:
-        sub *= 2
-    while sub < lo:
-        sub *= 2
-    return sub
+def profile_traffic(workload: str):
+    """HBM bytes per slot-fill launch from the committed rocprofv3 summary of this
+    workload (FETCH_SIZE and WRITE_SIZE per dispatch, scaled by the plain-copy
+    calibration it records), or None when the summary was taken on another
+    version of the kernel source."""
+    path = os.path.join(ROOT, "profiles", f"slot_fill_{workload}.md")
+    if not os.path.exists(path):
+        return None, None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if line.startswith("traffic-record:"):
+                for kv in line.split(":", 1)[1].split():
+                    k, v = kv.split("=", 1)
+                    fields[k] = v
+    if not fields or fields.get("kernel_sha") != _src_sha("slotfill.hip"):
+        return None, os.path.relpath(path, ROOT)
+    kib = 1024.0
+    b = (float(fields["fetch_kib"]) * float(fields["fetch_scale"]) +
+         float(fields["write_kib"]) * float(fields["write_scale"])) * kib
+    return b, os.path.relpath(path, ROOT)
 
 
 def _cpu_model() -> str:
@@ -107,6 +131,197 @@ def cpu_baseline(ids_host: np.ndarray, wl, budget_s: float):
                        f"({pairs} pairs), single host thread, {t_used:.1f} s"), outs
 
 
+def spare_slots(wl):
+    """Physical slot of every spare ordinal (rank-major; natives first in a rank)."""
+    out, s0 = [], 0
+    for nc_r, sc_r in zip(wl.native_count, wl.spare_count):
+        s0 += int(nc_r)
+        out.extend(range(s0, s0 + int(sc_r)))
+        s0 += int(sc_r)
+    return out
+
+
+def fill_rates(wl, phy2log_host: np.ndarray, fill_ms: np.ndarray):
+    """Slot-fill rates for the layers whose mean launch times are fill_ms, on the
+    per-slot rule (2 x W per filled slot) and on the bytes moved ((distinct
+    experts + filled slots) x W)."""
+    bpe = wl.bytes_per_expert
+    sp = phy2log_host[: len(fill_ms)][:, spare_slots(wl)]
+    filled = (sp >= 0).sum(axis=1).astype(np.float64)
+    distinct = np.array([len(np.unique(r[r >= 0])) for r in sp], np.float64)
+    t = float(np.mean(fill_ms)) * 1e-3
+    b = float((2 * bpe * filled).mean())
+    mb = float((bpe * (distinct + filled)).mean())
+    return {"ms": float(np.mean(fill_ms)), "bytes": b, "GBps": b / t / 1e9, "frac": b / t / 1e9 / HBM_PEAK_GBPS,
+            "moved_bytes": mb, "moved_GBps": mb / t / 1e9, "moved_frac": mb / t / 1e9 / HBM_PEAK_GBPS,
+            "filled": float(filled.mean()), "distinct": float(distinct.mean())}
+
+
+def moved_bytes_per_pair(N: int, P: int, E: int):
+    """Bytes per pair the histogram and the reroute move: with E <= 256 the
+    histogram writes a one-byte copy of each ID that the reroute reads instead
+    of the int32 ID (4 in + 1 out, 1 in + 4 out); otherwise 4 in, and 4 + 4.
+    Both also carry the count rows: one row of E + 1 int32 per sub-block,
+    written by the histogram and read by the reroute."""
+    h, r = (5.0, 5.0) if E <= 256 else (4.0, 8.0)
+    sub = ep.ep_sub_block_pairs(N, P, E)
+    rows = -(-N // sub) * (E + 1) * 4 / N if N else 0.0
+    return h + rows, r + rows
+
+
+def kernel_rates(pairs, hist_ms, rr_ms, serial_ms, plan_ms, path_ms, hist_moved, rr_moved):
+    g = lambda bpp, ms: bpp * pairs / (ms * 1e-3) / 1e9      # GB/s
+    return {
+        "path_GBps": g(PATH_BYTES_PER_PAIR, path_ms),
+        "path_frac": g(PATH_BYTES_PER_PAIR, path_ms) / HBM_PEAK_GBPS,
+        "path_stream_frac": g(PATH_BYTES_PER_PAIR, hist_ms + rr_ms) / HBM_PEAK_GBPS,
+        "path_serial_frac": g(PATH_BYTES_PER_PAIR, serial_ms) / HBM_PEAK_GBPS,
+        "per_kernel": {
+            "hist_ms": hist_ms, "reroute_ms": rr_ms, "plan_ms": plan_ms,
+            "hist_rule_bytes_per_pair": HIST_BYTES_PER_PAIR,
+            "hist_rule_frac": g(HIST_BYTES_PER_PAIR, hist_ms) / HBM_PEAK_GBPS,
+            "reroute_rule_bytes_per_pair": REROUTE_BYTES_PER_PAIR,
+            "reroute_rule_frac": g(REROUTE_BYTES_PER_PAIR, rr_ms) / HBM_PEAK_GBPS,
+            "hist_moved_bytes_per_pair": hist_moved,
+            "hist_moved_GBps": g(hist_moved, hist_ms), "hist_moved_frac": g(hist_moved, hist_ms) / HBM_PEAK_GBPS,
+            "reroute_moved_bytes_per_pair": rr_moved,
+            "reroute_moved_GBps": g(rr_moved, rr_ms),
+            "reroute_moved_frac": g(rr_moved, rr_ms) / HBM_PEAK_GBPS,
+        },
+    }
+
+
+def cpu_slot_fill(weights: torch.Tensor, phy2log_host: np.ndarray, wl, budget_s: float):
+    """The oracle's slot fill (a memcpy per filled spare slot) on the host over a
+    host copy of one layer's weights, for as many layers as fit the budget."""
+    import oracle
+
+    lay = oracle.Layout.from_workload(wl)
+    w = weights.cpu().view(torch.int16).numpy()
+    buf = np.empty((wl.num_spare, w.shape[1]), np.int16)
+    done, nbytes, t_used = 0, 0.0, 0.0
+    spare = spare_slots(wl)
+    for p in range(phy2log_host.shape[0]):
+        t0 = time.perf_counter()
+        oracle.slot_fill(w, phy2log_host[p], lay, buf)
+        t_used += time.perf_counter() - t0
+        nbytes += 2.0 * wl.bytes_per_expert * int((phy2log_host[p][spare] >= 0).sum())
+        done += 1
+        if t_used >= budget_s:
+            break
+    return {"value": nbytes / t_used, "unit": "B/s", "bytes_rule": FILL_RULE, "cores": 1, "kind": "oracle",
+            "sample": f"slot fill (memcpy per filled slot) of the first {done} of {phy2log_host.shape[0]} "
+                      f"layers over a host copy of one layer's weights, single host thread, {t_used:.1f} s"}
+
+
+def workload_summary(name: str, dev, cpu_bound: bool, fill_layers: int = 16):
+    """Compact numbers for one workload at full size: the path (fastest of one
+    stream and two chunks), each kernel alone, single-layer latencies, the slot
+    fill over its first layers, and the balance."""
+    wl = W.get(name)
+    P, N, E, S = wl.num_plans, wl.pairs_per_plan, wl.num_experts, wl.num_spare
+    ids = W.make_ids(wl, device=dev)
+    weights = W.make_weights(wl, device=dev)
+    lay = ep.Layout.from_workload(wl, device=dev)
+    slot = torch.empty((max(S, 1), weights.shape[1]), dtype=weights.dtype, device=dev)
+    fws = ep.slot_fill_workspace(lay, dev)
+    load = torch.empty((P, E), dtype=torch.int32, device=dev)
+    ws = ep.workspace(ids, lay)
+    status = torch.empty(P, dtype=torch.int32, device=dev)
+    plan = ep.alloc_plan(P, lay, dev)
+    phys = torch.empty_like(ids)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, reps=5):
+        fn()
+        xs = []
+        for _ in range(reps):
+            a = torch.cuda.Event(enable_timing=True); b = torch.cuda.Event(enable_timing=True)
+            a.record(stream); fn(); b.record(stream)
+            xs.append((a, b))
+        torch.cuda.synchronize()
+        return statistics.median(_elapsed(xs))
+
+    def serial():
+        ep.ep_load_histogram(ids, lay, load=load, ws=ws, status=status)
+        ep.ep_plan_quota(load, lay, out=plan, status=status)
+        ep.ep_reroute(ids, lay, plan.phy_quota, plan.log2phy, plan.logcnt, ws, phys_ids=phys)
+
+    t_serial = timed(serial)
+    best, best_chunks = t_serial, [P]
+    for first in sorted({round(0.37 * P), P // 2}):
+        if 1 <= first < P:
+            pp = ep.PathPipeline(lay, P, N, chunks=[first, P - first], device=dev)
+            t = timed(lambda: pp.run(ids, load, status, plan, phys))
+            if t < best * 0.98:
+                best, best_chunks = t, [first, P - first]
+            del pp
+    t_hist = timed(lambda: ep.ep_load_histogram(ids, lay, load=load, ws=ws, status=status))
+    t_plan = timed(lambda: ep.ep_plan_quota(load, lay, out=plan, status=status))
+    t_rr = timed(lambda: ep.ep_reroute(ids, lay, plan.phy_quota, plan.log2phy, plan.logcnt, ws, phys_ids=phys))
+    serial()
+    ids1, load1 = ids[:1], load[:1].clone()
+    pl1 = ep.alloc_plan(1, lay, dev)
+    t_plan1 = timed(lambda: ep.ep_plan_quota(load1, lay, out=pl1), reps=15) * 1e3
+    hm, rm = moved_bytes_per_pair(N, P, E)
+    kern = kernel_rates(P * N, t_hist, t_rr, t_serial, t_plan, best, hm, rm)
+
+    nf = min(P, fill_layers)
+    fms = []
+    if S > 0:
+        for _ in range(2):
+            ep.ep_slot_fill(weights, plan.phy2log[0], lay, slot, ws=fws)
+        ev = []
+        for rep in range(2):
+            for l in range(nf):
+                a = torch.cuda.Event(enable_timing=True); b = torch.cuda.Event(enable_timing=True)
+                a.record(stream); ep.ep_slot_fill(weights, plan.phy2log[l], lay, slot, ws=fws); b.record(stream)
+                ev.append((a, b))
+        torch.cuda.synchronize()
+        fms = np.array(_elapsed(ev)).reshape(2, nf).mean(axis=0)
+    fill = fill_rates(wl, plan.phy2log.cpu().numpy(), fms) if S > 0 else None
+
+    stats, imb, _ = ep.ep_balance_stats(load, plan.phy_quota, lay, want_rank_load=False)
+    imb_np = imb.cpu().numpy()
+    out = {
+        "path_pairs_per_s": P * N / (best * 1e-3), "path_ms": best, "path_chunks": best_chunks,
+        "path_one_stream_ms": t_serial,
+        "path_12B_frac": kern["path_frac"], "path_12B_frac_streaming_kernels": kern["path_stream_frac"],
+        "hist_ms": t_hist, "reroute_ms": t_rr,
+        "hist_rule_frac": kern["per_kernel"]["hist_rule_frac"],
+        "reroute_rule_frac": kern["per_kernel"]["reroute_rule_frac"],
+        "hist_moved_frac": kern["per_kernel"]["hist_moved_frac"],
+        "reroute_moved_frac": kern["per_kernel"]["reroute_moved_frac"],
+        "plan_us_per_layer_batched": t_plan * 1e3 / P, "plan_us_single_layer": t_plan1,
+        "imbalance_before_mean": float(imb_np[:, 0].mean()),
+        "imbalance_after_mean": float(imb_np[:, 1].mean()),
+        "imbalance_after_max": float(imb_np[:, 1].max()),
+        "status_nonzero": int((status != 0).sum().item()),
+        "planner_steps_max": int(plan.steps.max().item()),
+    }
+    if fill is not None:
+        out.update({"fill_ms_per_layer": fill["ms"], "fill_frac": fill["frac"],
+                    "fill_moved_frac": fill["moved_frac"], "fill_layers": nf,
+                    "filled_slots_mean": fill["filled"], "distinct_experts_mean": fill["distinct"]})
+    if cpu_bound:
+        # CPU side: the slot-count lower bound on the max rank load of every
+        # layer (no plan beats it), as an imbalance beside the planner's
+        from oracle.brute import slot_lower_bound
+        ld = load.cpu().numpy()
+        lbs = []
+        for p in range(P):
+            tot = int(ld[p].sum())
+            if tot > 0:
+                lbs.append((slot_lower_bound(ld[p], wl.num_ranks, S) * wl.num_ranks / tot, float(imb_np[p, 1])))
+        if lbs:
+            lb = np.array(lbs)
+            out["imbalance_lower_bound_mean"] = float(lb[:, 0].mean())
+            out["imbalance_after_over_bound_max"] = float((lb[:, 1] / lb[:, 0]).max())
+    del ids, weights, slot, ws, phys, load, plan
+    torch.cuda.empty_cache()
+    return out
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -120,6 +335,9 @@ def main(argv=None) -> int:
                          "fastest of one stream and a first chunk of 25/37/50%% of the plans, timed "
                          "during warmup), a number of equal chunks (1 = one stream), or "
                          "comma-separated sizes")
+    ap.add_argument("--workloads", default="all",
+                    help="after the headline: a compact measurement of the other workloads ('all', "
+                         "'none' or a comma-separated list of names)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args(argv)
@@ -158,6 +376,7 @@ def main(argv=None) -> int:
 
     lay = ep.Layout.from_workload(wl, device=dev)
     slot = torch.empty((S, weights.shape[1]), dtype=weights.dtype, device=dev)
+    fws = ep.slot_fill_workspace(lay, dev)
     load = torch.empty((P, E), dtype=torch.int32, device=dev)
     ws = ep.workspace(ids, lay)
     status = torch.empty(P, dtype=torch.int32, device=dev)
@@ -230,7 +449,7 @@ def main(argv=None) -> int:
         fills = []
         for l in range(P):
             x = ev()
-            ep.ep_slot_fill(weights, plan.phy2log[l], lay, slot)
+            ep.ep_slot_fill(weights, plan.phy2log[l], lay, slot, ws=fws)
             fills.append((x, ev()))
         if record:
             rec["path"].append((a, d)); rec["stats"].append((d, f)); rec["fill"].extend(fills)
@@ -251,22 +470,8 @@ def main(argv=None) -> int:
 
     st = stats.cpu().numpy()
     used = st[:, 3]
-    # algorithmic bytes of one slot fill: the weights of every distinct expert
-    # among the filled spare slots read once, every filled slot written once
-    # (an expert replicated into k slots of a layer is read once, written k times)
-    spare_idx, s0 = [], 0
-    for nc_r, sc_r in zip(wl.native_count, wl.spare_count):
-        s0 += int(nc_r)
-        spare_idx.extend(range(s0, s0 + int(sc_r)))
-        s0 += int(sc_r)
-    sp = plan.phy2log.cpu().numpy()[:, spare_idx]
-    distinct = np.array([len(np.unique(r[r >= 0])) for r in sp], np.float64)
-    fill_bytes = bpe * (distinct + used)                # per layer (launch)
     fill_ms = np.array(ms["fill"]).reshape(args.steps, P).mean(axis=0)
-    fill_gbps = float(fill_bytes.mean() / (fill_ms.mean() * 1e-3) / 1e9)
-    # the rate at which slot rows are filled, counted as a copy per slot would
-    # move them (read + write per filled slot); not HBM bytes
-    fill_eff_gbps = float((2 * bpe * used).mean() / (fill_ms.mean() * 1e-3) / 1e9)
+    fill = fill_rates(wl, plan.phy2log.cpu().numpy(), fill_ms)
     imb_np = imb.cpu().numpy()
 
     # single-plan latencies (one layer, as a real forward pass sees them)
@@ -306,20 +511,8 @@ def main(argv=None) -> int:
         ep.ep_plan_quota(load, lay, out=plan, status=status)
         ep.ep_reroute(ids, lay, plan.phy_quota, plan.log2phy, plan.logcnt, ws, phys_ids=phys)
     ph_serial = run_ms(serial, 5)
-    # algorithmic bytes per pair: with E <= 256 the histogram also writes a
-    # one-byte copy of each ID (4 in, 1 out), which the reroute reads instead
-    # of the int32 ID (1 in, 4 out); otherwise 4 in, and 4 in + 4 out
-    hist_bpp, rr_bpp = (5.0, 5.0) if E <= 256 else (4.0, 8.0)
-    # plus the per-sub-block counts the histogram hands to the reroute: one
-    # row of E + 1 int32 per sub-block (in-segment prefixes and segment
-    # totals), written by the histogram and read by the reroute (a sub-block's
-    # rank ranges end where the next one's start)
-    sub = _sub_pairs(N, P, E)
-    rows_pp = -(-N // sub) * (E + 1) * 4 / N
-    hist_bpp += rows_pp
-    rr_bpp += rows_pp
-    hist_gbps = hist_bpp * P * N / (ph_hist * 1e-3) / 1e9
-    rr_gbps = rr_bpp * P * N / (ph_rr * 1e-3) / 1e9
+    hist_moved, rr_moved = moved_bytes_per_pair(N, P, E)
+    kern = kernel_rates(P * N, ph_hist, ph_rr, ph_serial, ph_plan, path_ms, hist_moved, rr_moved)
 
     ids1 = ids[:1]
     load1 = load[:1].clone()
@@ -367,9 +560,7 @@ def main(argv=None) -> int:
                       "domain_imbalance_after_mean": float(imb_d_np[:, 1].mean()),
                       "domain_imbalance_after_max": float(imb_d_np[:, 1].max())})
 
-    traffic = None
-    if TRAFFIC and TRAFFIC.get("kernel_sha") == _src_sha("slotfill.hip"):
-        traffic = TRAFFIC["bytes_per_launch"]
+    traffic, traffic_src = profile_traffic(wl.name)
 
     out = {
         "metric": METRIC,
@@ -388,29 +579,31 @@ def main(argv=None) -> int:
                                f"{wl.tokens_per_rank} tokens/rank, {P} layers, {S} spare slots, "
                                f"expert 3x4096x1536 bf16",
                    "pairs_per_step": P * N, "plans_per_step": P},
-        "roofline": {"bound": "hbm", "kernel": "slot_fill_shared_kernel", "achieved": fill_gbps,
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": fill_gbps / HBM_PEAK_GBPS,
-                     "traffic": traffic,
-                     "bytes_per_launch": float(fill_bytes.mean()),
-                     "bytes_rule": "(distinct experts in filled spare slots + filled slots) x bytes_per_expert",
-                     "filled_slots_mean": float(used.mean()), "distinct_experts_mean": float(distinct.mean()),
-                     "per_slot_copy_equivalent_GBps": fill_eff_gbps,
-                     "launch_ms": float(fill_ms.mean())},
+        "roofline": {"bound": "hbm", "kernel": "fill_copy_kernel",
+                     "achieved": fill["GBps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": fill["frac"], "traffic": traffic,
+                     "bytes_rule": FILL_RULE, "bytes_per_launch": fill["bytes"],
+                     "achieved_moved": fill["moved_GBps"], "frac_moved": fill["moved_frac"],
+                     "moved_bytes_rule": FILL_MOVED_RULE, "moved_bytes_per_launch": fill["moved_bytes"],
+                     "traffic_source": traffic_src,
+                     "filled_slots_mean": fill["filled"], "distinct_experts_mean": fill["distinct"],
+                     "launch_ms": fill["ms"]},
+        "path": {"bytes_per_pair": PATH_BYTES_PER_PAIR,
+                 "overlapped_ms": path_ms, "overlapped_GBps": kern["path_GBps"],
+                 "overlapped_frac": kern["path_frac"],
+                 "streaming_kernels_ms": ph_hist + ph_rr, "streaming_kernels_frac": kern["path_stream_frac"],
+                 "one_stream_ms": ph_serial, "one_stream_frac": kern["path_serial_frac"]},
         "phases_ms_per_step": {"path": path_ms, "stats": statistics.mean(ms["stats"]),
                                "fill": float(fill_ms.sum())},
         "phases_ms_alone": {"hist": ph_hist, "plan": ph_plan, "reroute": ph_rr,
                             "path_one_stream": ph_serial},
         "path_chunks": [b - a for a, b in pipe.bounds] if pipe is not None else [P],
         "path_chunk_tuning_ms": tuning,
-        "kernels": {
-            "hist_bytes_per_pair": hist_bpp, "reroute_bytes_per_pair": rr_bpp,
-            "hist_GBps": hist_gbps, "hist_frac": hist_gbps / HBM_PEAK_GBPS,
-            "reroute_GBps": rr_gbps, "reroute_frac": rr_gbps / HBM_PEAK_GBPS,
-            "plan_us_per_layer_batched": ph_plan * 1e3 / P,
-            "plan_us_single_layer": lat_plan,
-            "hist_us_single_layer": lat_hist,
-            "reroute_us_single_layer": lat_rr,
-        },
+        "kernels": {**kern["per_kernel"],
+                    "plan_us_per_layer_batched": ph_plan * 1e3 / P,
+                    "plan_us_single_layer": lat_plan,
+                    "hist_us_single_layer": lat_hist,
+                    "reroute_us_single_layer": lat_rr},
         "next_rows": next_rows,
         "balance": {
             "imbalance_before_mean": float(imb_np[:, 0].mean()),
@@ -465,10 +658,40 @@ def main(argv=None) -> int:
             out["balance"]["lower_bound_layers"] = len(lbs)
             out["balance"]["imbalance_lower_bound_mean"] = float(lb[:, 0].mean())
             out["balance"]["imbalance_after_over_bound_max"] = float((lb[:, 1] / lb[:, 0]).max())
+        cb["slot_fill"] = cpu_slot_fill(weights, plan.phy2log.cpu().numpy(), wl, min(args.cpu_budget, 5.0))
         cb["host_threads_available"] = os.cpu_count()
         cb["host_cpu"] = _cpu_model()
     else:
         out["cpu_baseline"] = None
+
+    if args.workloads != "none":
+        del ids, weights, slot, ws, phys, dpos, dsrc
+        torch.cuda.empty_cache()
+        names = [n for n in W.WORKLOAD_ORDER if n != wl.name] if args.workloads == "all" \
+            else [n for n in args.workloads.split(",") if n]
+        block = {wl.name: {
+            "path_pairs_per_s": pairs_per_s, "path_ms": path_ms,
+            "path_chunks": out["path_chunks"], "path_12B_frac": kern["path_frac"],
+            "path_12B_frac_streaming_kernels": kern["path_stream_frac"],
+            "hist_ms": ph_hist, "reroute_ms": ph_rr,
+            "hist_rule_frac": kern["per_kernel"]["hist_rule_frac"],
+            "reroute_rule_frac": kern["per_kernel"]["reroute_rule_frac"],
+            "hist_moved_frac": kern["per_kernel"]["hist_moved_frac"],
+            "reroute_moved_frac": kern["per_kernel"]["reroute_moved_frac"],
+            "plan_us_per_layer_batched": ph_plan * 1e3 / P, "plan_us_single_layer": lat_plan,
+            "fill_ms_per_layer": fill["ms"], "fill_frac": fill["frac"], "fill_moved_frac": fill["moved_frac"],
+            "fill_layers": P, "filled_slots_mean": fill["filled"], "distinct_experts_mean": fill["distinct"],
+            "imbalance_before_mean": out["balance"]["imbalance_before_mean"],
+            "imbalance_after_mean": out["balance"]["imbalance_after_mean"],
+            "imbalance_after_max": out["balance"]["imbalance_after_max"],
+            "imbalance_lower_bound_mean": out["balance"].get("imbalance_lower_bound_mean"),
+            "imbalance_after_over_bound_max": out["balance"].get("imbalance_after_over_bound_max"),
+        }}
+        for n in names:
+            t0 = time.perf_counter()
+            block[n] = workload_summary(n, dev, cpu_bound=args.cpu_budget > 0)
+            print(f"[bench] workload {n}: {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
+        out["workloads"] = block
 
     print(json.dumps(out))
     return 0

@@ -23,7 +23,12 @@
  *
  * All EP ranks of one layer are simulated on one GPU: the rank is an array
  * axis.  One "plan" is one (microbatch, layer); calls take P plans at once.
-
+ *
+ * Departures from the plain five-call sketch of this interface: the layout is
+ * one packed device table built by ep_layout_init; ep_plan_quota also returns
+ * each plan's move count; ep_balance_stats returns four int64 columns plus the
+ * two imbalances as doubles (the move count and the step-cap flag come from
+ * the planner); ep_route_noalloc serves callers that cannot allocate.
  *
  * Conventions shared by every call
  *   - Pointers named as device data are device pointers owned by the caller;
@@ -62,6 +67,7 @@ enum {
 enum {
     EP_STATUS_BAD_ID = 1u,   /* an expert ID >= E was seen; such pairs count nowhere */
     EP_STATUS_STEP_CAP = 2u, /* the planner stopped at its step cap                  */
+    EP_STATUS_BAD_LOAD = 4u, /* the planner got a load < 0 or a total above INT32_MAX */
 };
 
 /*
@@ -125,6 +131,14 @@ int ep_layout_init(int32_t num_experts, int32_t num_ranks, const int32_t *native
  */
 size_t ep_workspace_bytes(int64_t pairs_per_plan, int32_t num_plans, int32_t num_experts);
 
+/*
+ * Pairs per sub-block for a launch of P plans of N pairs with E experts: the
+ * unit of work of one wave in the histogram, the reroute and the dispatch
+ * layout, and the unit of the workspace's count rows (one row of E + 1 int32
+ * per sub-block).  A power of two from 1024 up; 0 for invalid sizes.  For
+ * callers that account for the workspace's traffic; no call needs it.
+ */
+int64_t ep_sub_block_pairs(int64_t pairs_per_plan, int32_t num_plans, int32_t num_experts);
 
 /*
  * A1 -- exact per-expert load of every plan (UltraEP article, key designs:
@@ -168,7 +182,11 @@ int ep_load_histogram(const int32_t *topk_ids, int64_t pairs_per_plan, int32_t n
  *   logcnt    device int32 [P][E]: instances per expert (>= 1)
  *   log2phy   device int32 [P][E][rho]: instance slots in ascending order, -1 padded
  *   steps     device int32 [P] or NULL: committed moves
- *   status    device uint32 [P] or NULL: EP_STATUS_STEP_CAP is OR-ed in
+ *   status    device uint32 [P] or NULL: EP_STATUS_STEP_CAP and
+ *             EP_STATUS_BAD_LOAD are OR-ed in
+ * Every load must be >= 0 and a plan's total at most INT32_MAX (true of any
+ * histogram of fewer than 2^31 pairs).  A plan that breaks this makes no move:
+ * it keeps the native placement (quota = load) and gets EP_STATUS_BAD_LOAD.
  * Requires rho <= 64 (at most 64 instances of one expert), 1 <= P <= 65535,
  * and either R <= 64 with at most 8 natives and 16 spare slots per rank, or
  * tables that fit the generic kernel's 64 KiB of LDS (about 60 bytes per rank
@@ -206,6 +224,41 @@ int ep_reroute(const int32_t *topk_ids, int64_t pairs_per_plan, int32_t num_plan
                ep_stream_t stream);
 
 /*
+ * A1 -> A2 -> A3 over a batch of plans (e.g. every MoE layer of a microbatch)
+ * cut into chunks that overlap across three streams: one planner launch lasts
+ * about as long as its slowest plan, so the planner of chunk c runs while the
+ * histogram of chunk c + 1 streams, and the reroute of chunk c while the
+ * planner of chunk c + 1 runs.  The outputs are exactly those of
+ * ep_load_histogram, ep_plan_quota and ep_reroute made in order on one stream
+ * (arguments and layouts as there, P plans).
+ *   chunk_plans  host int32 [num_chunks]: plans per chunk, each >= 1, summing
+ *                to P; 1 <= num_chunks <= EP_MAX_CHUNKS
+ *   ws           device, >= ep_pipeline_workspace_bytes(N, chunk_plans,
+ *                num_chunks, E) bytes, 16-byte aligned: one histogram
+ *                workspace per chunk
+ *   stream       the caller's stream: the chain starts after the work already
+ *                enqueued there and later work there waits for all of it;
+ *                histograms run on it
+ *   plan_stream, reroute_stream  two further streams of the caller (distinct
+ *                from each other and from `stream`, default priority):
+ *                planners and reroutes run on them
+ *   events       2 + 2 * num_chunks events of the caller (hipEvent_t, e.g.
+ *                created with hipEventDisableTiming), recorded and waited on
+ *                here; no other work may use them until the chain completes
+ * Returns EP_ERR_INVALID_ARG (nothing enqueued) for bad arguments, including
+ * any that one of the three calls would reject for a chunk.
+ */
+#define EP_MAX_CHUNKS 16
+size_t ep_pipeline_workspace_bytes(int64_t pairs_per_plan, const int32_t *chunk_plans, int32_t num_chunks,
+                                   int32_t num_experts);
+int ep_route_pipelined(const int32_t *topk_ids, int64_t pairs_per_plan, int32_t num_plans,
+                       const ep_layout_t *layout, const int32_t *chunk_plans, int32_t num_chunks,
+                       int32_t *load, uint32_t *status, int32_t *phy2log, int32_t *phy_quota,
+                       int32_t *logcnt, int32_t *log2phy, int32_t *steps, int32_t *phys_ids, void *ws,
+                       size_t ws_bytes, ep_stream_t stream, ep_stream_t plan_stream,
+                       ep_stream_t reroute_stream, void *const *events);
+
+/*
  * Next row after A3 -- dispatch layout for the token all-to-all (EPLB
  * tutorial, EPLB / DeepEP section: dispatch sends each pair to its physical
  * replica; combine gathers results back to the logical expert).  Pairs are
@@ -234,14 +287,24 @@ int ep_dispatch_layout(const int32_t *topk_ids, int64_t pairs_per_plan, int32_t 
  * occupies a spare slot into that slot's row of the cross-layer slot buffer
  * (UltraEP article, key designs: reserved slots, weight buffers reused across
  * layers).  One plan (one layer) per call; empty spare slots are not written.
+ * Each distinct expert is read once and stored into every slot that holds it.
  *   expert_weights device [E][bytes_per_expert], one layer (16-byte aligned)
  *   phy2log        device int32 [Phi], that layer's plan
  *   slot_buf       device [S][bytes_per_expert] (16-byte aligned)
+ *   ws             device, ep_slot_fill_workspace_bytes(layout) bytes (16-byte
+ *                  aligned), or NULL: with it the call first lists the plan's
+ *                  distinct experts and their slots there (a one-workgroup
+ *                  kernel) and then streams each expert's weights in address
+ *                  order, the faster form; without it every workgroup finds
+ *                  its slot's expert itself.  The workspace holds no state
+ *                  between calls; calls in flight at once need their own.
  * bytes_per_expert must be a positive multiple of 16.  A spare slot whose
  * phy2log entry lies outside [0, E) is empty: its row is not written.
  */
+size_t ep_slot_fill_workspace_bytes(const ep_layout_t *layout);
 int ep_slot_fill(const void *expert_weights, int64_t bytes_per_expert, const int32_t *phy2log,
-                 const ep_layout_t *layout, void *slot_buf, ep_stream_t stream);
+                 const ep_layout_t *layout, void *slot_buf, void *ws, size_t ws_bytes,
+                 ep_stream_t stream);
 
 /*
  * Next row -- replica gradient reduction in backward (UltraEP article, key

@@ -25,6 +25,7 @@ EP_ERR_TOO_LARGE = -3
 EP_NOALLOC_SCRATCH_BYTES = 64 << 20
 EP_STATUS_BAD_ID = 1
 EP_STATUS_STEP_CAP = 2
+EP_STATUS_BAD_LOAD = 4
 
 
 class EPBalanceError(RuntimeError):
@@ -62,19 +63,27 @@ def lib() -> ctypes.CDLL:
         L.ep_layout_init.argtypes = [i32, i32, vp, vp, vp, vp, sz, lp]
         L.ep_workspace_bytes.argtypes = [i64, i32, i32]
         L.ep_workspace_bytes.restype = sz
+        L.ep_sub_block_pairs.argtypes = [i64, i32, i32]
+        L.ep_sub_block_pairs.restype = i64
         L.ep_load_histogram.argtypes = [vp, i64, i32, lp, vp, vp, sz, vp, vp]
         L.ep_plan_quota.argtypes = [vp, i32, lp, vp, vp, vp, vp, vp, vp, vp]
         L.ep_reroute.argtypes = [vp, i64, i32, lp, vp, vp, vp, vp, sz, vp, vp]
-        L.ep_slot_fill.argtypes = [vp, i64, vp, lp, vp, vp]
+        L.ep_slot_fill.argtypes = [vp, i64, vp, lp, vp, vp, sz, vp]
+        L.ep_slot_fill_workspace_bytes.argtypes = [lp]
+        L.ep_slot_fill_workspace_bytes.restype = sz
         L.ep_dispatch_layout.argtypes = [vp, i64, i32, lp, vp, vp, vp, vp, sz, vp, vp, vp, vp]
         L.ep_replica_grad_reduce.argtypes = [vp, i64, vp, vp, vp, lp, vp]
         L.ep_balance_stats.argtypes = [vp, vp, i32, lp, vp, vp, vp, vp]
         L.ep_route_noalloc.argtypes = [vp, i64, i32, lp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.ep_pipeline_workspace_bytes.argtypes = [i64, ctypes.POINTER(i32), i32, i32]
+        L.ep_pipeline_workspace_bytes.restype = sz
+        L.ep_route_pipelined.argtypes = [vp, i64, i32, lp, ctypes.POINTER(i32), i32, vp, vp, vp, vp, vp, vp, vp,
+                                         vp, vp, sz, vp, vp, vp, ctypes.POINTER(vp)]
         L.ep_status_string.argtypes = [ctypes.c_int]
         L.ep_status_string.restype = ctypes.c_char_p
         for f in ("ep_layout_init", "ep_load_histogram", "ep_plan_quota", "ep_reroute",
                   "ep_slot_fill", "ep_balance_stats", "ep_dispatch_layout", "ep_replica_grad_reduce",
-                  "ep_route_noalloc"):
+                  "ep_route_noalloc", "ep_route_pipelined"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -185,6 +194,10 @@ class Layout:
 
 def ep_workspace_bytes(pairs_per_plan: int, num_plans: int, num_experts: int) -> int:
     return int(lib().ep_workspace_bytes(pairs_per_plan, num_plans, num_experts))
+
+
+def ep_sub_block_pairs(pairs_per_plan: int, num_plans: int, num_experts: int) -> int:
+    return int(lib().ep_sub_block_pairs(int(pairs_per_plan), int(num_plans), int(num_experts)))
 
 
 def workspace(topk_ids: torch.Tensor, layout: Layout) -> torch.Tensor:
@@ -314,9 +327,22 @@ def ep_route_noalloc(topk_ids: torch.Tensor, layout: Layout, load: torch.Tensor,
     return load, status, plan, phys_ids
 
 
+def ep_slot_fill_workspace_bytes(layout: Layout) -> int:
+    return int(lib().ep_slot_fill_workspace_bytes(layout.ref()))
+
+
+def slot_fill_workspace(layout: Layout, device) -> torch.Tensor:
+    """A workspace for ep_slot_fill (reusable by consecutive calls on one stream)."""
+    return torch.empty(max(ep_slot_fill_workspace_bytes(layout), 16), dtype=torch.uint8, device=device)
+
+
 def ep_slot_fill(expert_weights: torch.Tensor, phy2log: torch.Tensor, layout: Layout,
-                 slot_buf: torch.Tensor, stream=None) -> torch.Tensor:
-    """expert_weights [E][...] (one layer), phy2log int32 [Phi] (one plan), slot_buf [S][...]."""
+                 slot_buf: torch.Tensor, ws: Optional[torch.Tensor] = None, stream=None,
+                 use_ws: bool = True) -> torch.Tensor:
+    """expert_weights [E][...] (one layer), phy2log int32 [Phi] (one plan), slot_buf [S][...].
+
+    ws: the fill-list workspace (slot_fill_workspace); one is taken from torch's
+    allocator when not given, unless use_ws is False (the form without a list)."""
     if not (expert_weights.is_cuda and slot_buf.is_cuda and expert_weights.is_contiguous()
             and slot_buf.is_contiguous()):
         raise EPBalanceError("weights and slot buffer must be contiguous device tensors")
@@ -327,8 +353,13 @@ def ep_slot_fill(expert_weights: torch.Tensor, phy2log: torch.Tensor, layout: La
     bpe = total // layout.num_experts
     if slot_buf.numel() * slot_buf.element_size() < layout.num_spare * bpe:
         raise EPBalanceError("slot_buf is smaller than S * bytes_per_expert")
+    if ws is None and use_ws:
+        ws = slot_fill_workspace(layout, expert_weights.device)
+    if ws is not None and not (ws.is_cuda and ws.is_contiguous()):
+        raise EPBalanceError("ws must be a contiguous device tensor")
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     rc = lib().ep_slot_fill(_ptr(expert_weights), bpe, _ptr(phy2log), layout.ref(), _ptr(slot_buf),
-                            _stream(stream))
+                            _ptr(ws), nbytes, _stream(stream))
     _check(rc, "ep_slot_fill")
     return slot_buf
 
@@ -360,14 +391,18 @@ def plan_rows(plan: PlanOut, a: int, b: int) -> PlanOut:
                    plan.steps[a:b])
 
 
+EP_MAX_CHUNKS = 16
+
+
 class PathPipeline:
     """hist -> plan -> reroute over a batch of plans, cut into chunks of plans and
-    overlapped across three streams: the planner of chunk c runs while the
-    histogram of chunk c + 1 streams, and the reroute of chunk c while the planner
-    of chunk c + 1 runs.  The outputs are those of the same calls made in order
-    on one stream.  Owns its streams, events and per-chunk workspaces; the caller
-    owns inputs and outputs.  run() only enqueues: it is ordered after earlier
-    work on the caller's stream, and later work on that stream waits for it."""
+    overlapped across three streams by the library's ep_route_pipelined: the
+    planner of chunk c runs while the histogram of chunk c + 1 streams, and the
+    reroute of chunk c while the planner of chunk c + 1 runs.  The outputs are
+    those of the same calls made in order on one stream.  Owns the two side
+    streams, the events and the per-chunk workspaces; the caller owns inputs and
+    outputs.  run() only enqueues: it is ordered after earlier work on the
+    caller's stream, and later work on that stream waits for it."""
 
     def __init__(self, layout: Layout, num_plans: int, pairs_per_plan: int, chunks=2, device=None):
         """chunks: a number of equal chunks, or the list of chunk sizes (plans).
@@ -382,8 +417,8 @@ class PathPipeline:
             sizes = [base + (1 if c < extra else 0) for c in range(n)]
         else:
             sizes = [int(x) for x in chunks]
-        if not sizes or min(sizes) < 1 or sum(sizes) != int(num_plans):
-            raise ValueError(f"chunk sizes {sizes} do not split {num_plans} plans")
+        if not sizes or min(sizes) < 1 or sum(sizes) != int(num_plans) or len(sizes) > EP_MAX_CHUNKS:
+            raise ValueError(f"chunk sizes {sizes} do not split {num_plans} plans (at most {EP_MAX_CHUNKS} chunks)")
         self.bounds = []
         a = 0
         for s in sizes:
@@ -391,41 +426,35 @@ class PathPipeline:
             a += s
         self.layout = layout
         self.num_plans, self.pairs_per_plan = int(num_plans), int(pairs_per_plan)
-        self.ws = []
-        for a, b in self.bounds:
-            nbytes = ep_workspace_bytes(self.pairs_per_plan, b - a, layout.num_experts)
-            self.ws.append(torch.empty(max(16, nbytes), dtype=torch.uint8, device=dev))
-        # default-priority streams
-        self.s_hist, self.s_plan, self.s_rr = (torch.cuda.Stream(device=dev) for _ in range(3))
-        self.e_start, self.e_done = torch.cuda.Event(), torch.cuda.Event()
-        self.e_hist = [torch.cuda.Event() for _ in self.bounds]
-        self.e_plan = [torch.cuda.Event() for _ in self.bounds]
+        self._sizes = (ctypes.c_int32 * len(sizes))(*sizes)
+        nbytes = lib().ep_pipeline_workspace_bytes(self.pairs_per_plan, self._sizes, len(sizes), layout.num_experts)
+        self.ws = torch.empty(max(16, nbytes), dtype=torch.uint8, device=dev)
+        # default-priority side streams; events created (by a first record) up front
+        self.s_plan, self.s_rr = torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev)
+        self.events = [torch.cuda.Event() for _ in range(2 + 2 * len(sizes))]
+        cur = torch.cuda.current_stream(dev)
+        for e in self.events:
+            e.record(cur)
+        self._ev = (ctypes.c_void_p * len(self.events))(*[e.cuda_event for e in self.events])
 
     def run(self, topk_ids: torch.Tensor, load: torch.Tensor, status: torch.Tensor, plan: PlanOut,
             phys_ids: torch.Tensor, stream=None):
         if tuple(topk_ids.shape) != (self.num_plans, self.pairs_per_plan):
             raise ValueError(f"topk_ids shape {tuple(topk_ids.shape)} != "
                              f"({self.num_plans}, {self.pairs_per_plan})")
-        main = stream if stream is not None else torch.cuda.current_stream()
-        lay = self.layout
-        self.e_start.record(main)
-        for s in (self.s_hist, self.s_plan, self.s_rr):
-            s.wait_event(self.e_start)
-        for c, (a, b) in enumerate(self.bounds):
-            ep_load_histogram(topk_ids[a:b], lay, load=load[a:b], ws=self.ws[c], status=status[a:b],
-                              stream=self.s_hist)
-            self.e_hist[c].record(self.s_hist)
-        for c, (a, b) in enumerate(self.bounds):
-            self.s_plan.wait_event(self.e_hist[c])
-            ep_plan_quota(load[a:b], lay, out=plan_rows(plan, a, b), status=status[a:b],
-                          stream=self.s_plan)
-            self.e_plan[c].record(self.s_plan)
-        for c, (a, b) in enumerate(self.bounds):
-            self.s_rr.wait_event(self.e_plan[c])
-            ep_reroute(topk_ids[a:b], lay, plan.phy_quota[a:b], plan.log2phy[a:b], plan.logcnt[a:b],
-                       self.ws[c], phys_ids=phys_ids[a:b], stream=self.s_rr)
-        self.e_done.record(self.s_rr)
-        main.wait_event(self.e_done)
+        P, N, lay = self.num_plans, self.pairs_per_plan, self.layout
+        _dev(topk_ids, torch.int32, "topk_ids")
+        _arg(load, torch.int32, (P, lay.num_experts), "load"); _arg(status, torch.int32, (P,), "status")
+        _arg(plan.phy2log, torch.int32, (P, lay.num_phys), "phy2log")
+        _plan_args(lay, P, plan.phy_quota, plan.log2phy, plan.logcnt)
+        _arg(plan.steps, torch.int32, (P,), "steps")
+        _arg(phys_ids, torch.int32, (P, N), "phys_ids")
+        rc = lib().ep_route_pipelined(_ptr(topk_ids), N, P, lay.ref(), self._sizes, len(self.bounds), _ptr(load),
+                                      _ptr(status), _ptr(plan.phy2log), _ptr(plan.phy_quota), _ptr(plan.logcnt),
+                                      _ptr(plan.log2phy), _ptr(plan.steps), _ptr(phys_ids), _ptr(self.ws),
+                                      self.ws.numel(), _stream(stream), ctypes.c_void_p(self.s_plan.cuda_stream),
+                                      ctypes.c_void_p(self.s_rr.cuda_stream), self._ev)
+        _check(rc, "ep_route_pipelined")
 
 
 def run_path(topk_ids: torch.Tensor, layout: Layout, stream=None):

@@ -13,7 +13,7 @@ using namespace ep;
 
 namespace {
 
-constexpr size_t kMaxLds = 65536;
+constexpr size_t kMaxLds = kLdsMax;
 constexpr int64_t kMaxPairs = 0x7fffffffLL;
 constexpr int32_t kMaxPlans = 65535;
 
@@ -159,6 +159,11 @@ size_t ep_workspace_bytes(int64_t pairs_per_plan, int32_t num_plans, int32_t num
     return ws_bytes(pairs_per_plan, num_plans, num_experts);
 }
 
+int64_t ep_sub_block_pairs(int64_t pairs_per_plan, int32_t num_plans, int32_t num_experts) {
+    if (pairs_per_plan < 0 || num_plans < 1 || num_experts < 1) return 0;
+    return sub_pairs(pairs_per_plan, num_plans, num_experts);
+}
+
 int ep_load_histogram(const int32_t *topk_ids, int64_t N, int32_t P, const ep_layout_t *layout,
                       int32_t *load, void *ws, size_t ws_size, uint32_t *status,
                       ep_stream_t stream) {
@@ -220,15 +225,24 @@ int ep_replica_grad_reduce(float *native_grads, int64_t elems_per_expert, const 
                                      as_stream(stream)));
 }
 
+size_t ep_slot_fill_workspace_bytes(const ep_layout_t *layout) {
+    if (!layout_ok(layout)) return 0;
+    return fill_ws_bytes(layout->num_spare);
+}
+
 int ep_slot_fill(const void *expert_weights, int64_t bytes_per_expert, const int32_t *phy2log,
-                 const ep_layout_t *layout, void *slot_buf, ep_stream_t stream) {
+                 const ep_layout_t *layout, void *slot_buf, void *ws, size_t ws_size, ep_stream_t stream) {
     if (!layout_ok(layout) || !phy2log || bytes_per_expert <= 0 || bytes_per_expert % 16 != 0)
         return EP_ERR_INVALID_ARG;
     if (layout->num_spare == 0) return EP_OK;
     if (!expert_weights || !slot_buf || !aligned(expert_weights, 16) || !aligned(slot_buf, 16))
         return EP_ERR_INVALID_ARG;
     if (layout->num_spare > kMaxPlans) return EP_ERR_INVALID_ARG;
-    return hip_rc(launch_slot_fill(expert_weights, bytes_per_expert, phy2log, *layout, slot_buf,
+    // a workspace is optional; one too small, or misaligned, is an error
+    const size_t need = fill_ws_bytes(layout->num_spare);
+    if (ws && (ws_size < need || !aligned(ws, 16))) return EP_ERR_INVALID_ARG;
+    int32_t *list = ws && need > 0 ? static_cast<int32_t *>(ws) : nullptr;
+    return hip_rc(launch_slot_fill(expert_weights, bytes_per_expert, phy2log, *layout, slot_buf, list,
                                    as_stream(stream)));
 }
 

@@ -139,8 +139,29 @@ __global__ __launch_bounds__(W *kWave) void dispatch_kernel(
             acc += q;
         }
     }
-    if (blockIdx.x == 0)
+    if (blockIdx.x == 0) {
         for (int s = threadIdx.x; s <= Phi; s += W * kWave) slot_offsets[(int64_t)p * (Phi + 1) + s] = soff[s];
+        // an instance whose quota range reaches past its expert's load (a plan
+        // whose quotas exceed the loads) leaves positions no pair takes: they
+        // get -1 here (none for plans whose quotas equal the loads); the pairs'
+        // own positions and the tail past the total are written below
+        const int32_t *tot = ws + ((int64_t)p * (nsb + nseg + 1) + nsb + nseg) * E1;
+        int32_t *srow = dsrc + (int64_t)p * N;
+        for (int e = threadIdx.x; e < E; e += W * kWave) {
+            const int f = rfirst[e], n = rcnt[e];
+            const int32_t le = tot[e];
+            int32_t prev = 0;
+            for (int t = 0; t < n; t++) {
+                const int2 in = inst[f + t];
+                if (in.y != (int32_t)0x80000000)
+                    for (int64_t j = prev > le ? prev : le; j < in.x; j++) {
+                        const int64_t pos = j + in.y;
+                        if (pos >= 0 && pos < N) srow[pos] = -1;
+                    }
+                prev = in.x;
+            }
+        }
+    }
     __syncthreads();
 
     // each wave walks the plan's sub-blocks with a stride of the plan's waves,
@@ -228,7 +249,12 @@ __global__ __launch_bounds__(W *kWave) void dispatch_kernel(
         const int32_t t = __builtin_nontemporal_load(src + (i < end ? i : last));
         nxt[u] = i < end ? t : -1;
     }
-    for (int64_t g = begin; g < end; g += U * kWave) {
+    // whole groups of U columns store every pair's position unconditionally:
+    // a store under a branch leaves the compiler unable to count the stores
+    // issued after the prefetched ID loads, and its wait for those loads then
+    // also waits for every store (stores and loads share one counter here)
+    auto group = [&](int64_t g, auto fullc) {
+        constexpr bool FULL = decltype(fullc)::value;
         int32_t v[U];
 #pragma unroll
         for (int u = 0; u < U; u++) {
@@ -272,7 +298,7 @@ __global__ __launch_bounds__(W *kWave) void dispatch_kernel(
                     if (c.kf & kSplitFlag) pos = position_of(inst, rfirst[xi], rcnt[xi], c.base + k);
                     if (STAGED) stage[valid ? off + k : sub] = (uint16_t)(i - begin);
                     else if (pos >= 0 && pos < N) src_out[pos] = (int32_t)i;
-                    if (i < end) __builtin_nontemporal_store(pos, pos_out + i);
+                    if (FULL || i < end) __builtin_nontemporal_store(pos, pos_out + i);
                 };
                 place(ca, ia, va, offa, ka, g + u * kWave + lane);
                 place(cb, ib, vb, offb, kb, g + (u + 1) * kWave + lane);
@@ -298,10 +324,19 @@ __global__ __launch_bounds__(W *kWave) void dispatch_kernel(
                 if (cur.kf & kSplitFlag) pos = position_of(inst, rfirst[xi], rcnt[xi], cur.base + k);
                 if (STAGED) stage[valid ? off + k : sub] = (uint16_t)(i - begin);
                 else if (pos >= 0 && pos < N) src_out[pos] = (int32_t)i;
-                if (i < end) __builtin_nontemporal_store(pos, pos_out + i);
+                if (FULL || i < end) __builtin_nontemporal_store(pos, pos_out + i);
                 wave_lds_fence();
             }
         }
+    };
+    // (only in the staged form: the non-staged one stores dispatch_src under a
+    // branch anyway, and the second copy of the loop costs it registers and
+    // resident waves: 7 % slower on the stress batch)
+    {
+        int64_t g = begin;
+        if constexpr (STAGED)
+            for (; g + U * kWave <= end; g += U * kWave) group(g, std::true_type{});
+        for (; g < end; g += U * kWave) group(g, std::false_type{});
     }
     if (STAGED) {
         // staged slots in order, 64 per step: slot t belongs to the non-empty
@@ -354,8 +389,8 @@ __global__ __launch_bounds__(W *kWave) void dispatch_kernel(
 
 int pick_dispatch_waves(int E, int Phi, int64_t stage, bool pair) {
     for (int w = 4; w >= 1; w >>= 1)
-        if (dispatch_lds_bytes(E, Phi, w, stage, pair) <= 65536) return w;
-    return 0;
+        if (dispatch_lds_bytes(E, Phi, w, stage, pair) <= kLdsPreferred) return w;
+    return dispatch_lds_bytes(E, Phi, 1, stage, pair) <= kLdsMax ? 1 : 0;
 }
 
 }  // namespace
@@ -404,7 +439,7 @@ hipError_t launch_dispatch(const int32_t *ids, int64_t N, int32_t P, const ep_la
     // the columns (GLM-4.5-like and stress batches 25 % and 8 % faster), but its
     // larger cells cost the 128-expert layout resident waves (17 % slower); so
     // pairs above 128 experts, when their cells fit in LDS.
-    const bool pair = E > 128 && pick_dispatch_waves(E, Phi, 0, true) > 0;
+    const bool pair = E > 128 && dispatch_lds_bytes(E, Phi, 1, 0, true) <= kLdsPreferred;
     auto best_waves = [&](bool st, int &w_out) {
         const int w0 = pick_dispatch_waves(E, Phi, st ? sub : 0, pair);
         int best = w0, waves = -1;

@@ -10,6 +10,12 @@
 namespace ep {
 
 constexpr int kWave = 64;
+// LDS per workgroup on gfx950 (160 KB per CU, all of it addressable by one
+// workgroup), and the budget the launchers prefer so that several workgroups
+// share a CU; a shape that needs more than the preferred budget runs with
+// fewer, larger-LDS workgroups
+constexpr size_t kLdsMax = 160 * 1024;
+constexpr size_t kLdsPreferred = 64 * 1024;
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -350,8 +356,10 @@ hipError_t launch_dispatch(const int32_t *ids, int64_t N, int32_t P, const ep_la
 size_t dispatch_lds_bytes(int E, int Phi, int waves, int64_t stage_pairs, bool pair);
 hipError_t launch_grad_reduce(float *native, int64_t n, const float *slot, const int32_t *log2phy,
                               const int32_t *logcnt, const ep_layout_t &L, hipStream_t s);
+// ws: the fill-list workspace (fill_ws_bytes(S) bytes) or null
 hipError_t launch_slot_fill(const void *w, int64_t bytes_per_expert, const int32_t *phy2log,
-                            const ep_layout_t &L, void *buf, hipStream_t s);
+                            const ep_layout_t &L, void *buf, int32_t *ws, hipStream_t s);
+size_t fill_ws_bytes(int32_t S);
 hipError_t launch_stats(const int32_t *load, const int32_t *phy_quota, int32_t P,
                         const ep_layout_t &L, int64_t *stats, double *imbalance,
                         int32_t *rank_load, hipStream_t s);

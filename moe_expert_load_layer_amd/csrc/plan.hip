@@ -68,7 +68,20 @@ __global__ __launch_bounds__(kWave) void plan_kernel_generic(const int32_t *__re
     for (int r = lane; r <= R; r += kWave) rfirst[r] = a.T.rank_first[r];
     for (int r = lane; r < R; r += kWave) { rnat[r] = a.T.rank_nat[r]; stamp[r] = -1; }
     for (int s = lane; s < Phi; s += kWave) { owner[s] = a.T.slot_home[s]; srank[s] = a.T.slot_rank[s]; }
-    for (int e = lane; e < E; e += kWave) { hslot[e] = a.T.home_slot[e]; ld[e] = lp[e]; icnt[e] = 1; }
+    // loads must be >= 0 with a total that fits int32 (every quota and rank
+    // load is then a partial sum of them); a plan that breaks this is flagged
+    // and keeps its native placement
+    int64_t lsum = 0;
+    bool lneg = false;
+    for (int e = lane; e < E; e += kWave) {
+        hslot[e] = a.T.home_slot[e];
+        const int32_t v = lp[e];
+        ld[e] = v;
+        icnt[e] = 1;
+        lsum += v;
+        lneg |= v < 0;
+    }
+    const bool bad_load = __ballot(lneg) != 0 || readlane_i64(wave_incl_scan_i64(lsum), kWave - 1) > 0x7fffffffLL;
     for (int o = lane; o < S; o += kWave) sslot[o] = a.T.spare_slot[o];
     __syncthreads();
     for (int s = lane; s < Phi; s += kWave) {
@@ -173,7 +186,7 @@ __global__ __launch_bounds__(kWave) void plan_kernel_generic(const int32_t *__re
 
     const int cap = 2 * S + R;
     int steps = 0, cap_hit = 0;
-    for (;;) {
+    for (; !bad_load;) {
         if (steps == cap) { cap_hit = 1; break; }
         uint64_t key = 0;
         for (int r = lane; r < R; r += kWave) {
@@ -256,7 +269,8 @@ __global__ __launch_bounds__(kWave) void plan_kernel_generic(const int32_t *__re
     }
     if (lane == 0) {
         if (steps_out) steps_out[p] = steps;
-        if (status && cap_hit) status[p] |= (uint32_t)EP_STATUS_STEP_CAP;
+        const uint32_t flags = (cap_hit ? (uint32_t)EP_STATUS_STEP_CAP : 0u) | (bad_load ? (uint32_t)EP_STATUS_BAD_LOAD : 0u);
+        if (status && flags) status[p] |= flags;
     }
 }
 
@@ -332,13 +346,23 @@ __global__ __launch_bounds__(kWave) void plan_kernel_lanes(const int32_t *__rest
     for (int j = 0; j < SPR; j++) { sp_owner[j] = -1; sp_q[j] = 0; }
     for (int e = lane; e < E; e += kWave) { emask[e] = 0; edirty[e] = 0; }
     int rl = 0;
+    int64_t lsum = 0;
+    bool lneg = false;
 #pragma unroll
-    for (int i = 0; i < NPR; i++) rl += nat_ld[i];
+    for (int i = 0; i < NPR; i++) {
+        rl += nat_ld[i];
+        lsum += nat_ld[i];
+        lneg |= nat_ld[i] < 0;
+    }
+    // loads must be >= 0 with a total that fits int32 (every quota and rank
+    // load is then a partial sum of them); a plan that breaks this is flagged
+    // and keeps its native placement
+    const bool bad_load = __ballot(lneg) != 0 || readlane_i64(wave_incl_scan_i64(lsum), kWave - 1) > 0x7fffffffLL;
     __syncthreads();
 
     const int cap = 2 * S + R;
     int steps = 0, cap_hit = 0;
-    for (;;) {
+    for (; !bad_load;) {
         if (steps == cap) { cap_hit = 1; break; }
         // hottest rank (lowest index on ties)
         const int vmax = wave_max_i32(is_rank ? rl : -1);
@@ -535,7 +559,8 @@ __global__ __launch_bounds__(kWave) void plan_kernel_lanes(const int32_t *__rest
     }
     if (lane == 0) {
         if (steps_out) steps_out[p] = steps;
-        if (status && cap_hit) status[p] |= (uint32_t)EP_STATUS_STEP_CAP;
+        const uint32_t flags = (cap_hit ? (uint32_t)EP_STATUS_STEP_CAP : 0u) | (bad_load ? (uint32_t)EP_STATUS_BAD_LOAD : 0u);
+        if (status && flags) status[p] |= flags;
     }
 }
 
@@ -561,7 +586,7 @@ int plan_lanes_cfg(const ep_layout_t &L) {
     const int mn = L.max_rank_natives > 0 ? L.max_rank_natives : 1;
     const int npr = (mn > 4 && mn <= 6) ? 6 : pow2_at_least(mn);
     const int spr = pow2_at_least(L.max_rank_spares > 0 ? L.max_rank_spares : 1);
-    if (npr > 8 || spr > 16 || lanes_lds_bytes(L) > 65536) return 0;
+    if (npr > 8 || spr > 16 || lanes_lds_bytes(L) > kLdsMax) return 0;
     return npr * 32 + spr;
 }
 

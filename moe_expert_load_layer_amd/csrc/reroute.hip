@@ -385,8 +385,8 @@ __global__ __launch_bounds__(W *kWave, BYTES ? 7 : 1) void reroute_kernel(
 
 int pick_waves(int E, int Phi) {
     for (int w = EP_RR_MAX_WAVES; w >= 1; w >>= 1)
-        if (reroute_lds_bytes(E, Phi, w) <= 65536) return w;
-    return 0;
+        if (reroute_lds_bytes(E, Phi, w) <= kLdsPreferred) return w;
+    return reroute_lds_bytes(E, Phi, 1) <= kLdsMax ? 1 : 0;
 }
 
 }  // namespace

@@ -2,47 +2,138 @@
 // designs: replicas live in slots reserved per rank, and one slot buffer is
 // reused by every layer).  For the o-th spare slot s with phy2log[s] = e >= 0,
 // expert e's weights are copied into row o of the slot buffer; empty slots are
-// not written.  A pure HBM-to-HBM stream of 16-byte loads and stores, each
-// workgroup of 256 threads moving one 16 KiB chunk.
+// not written.  A pure HBM-to-HBM stream of 16-byte loads and stores.
 //
-// A hot expert often has several replicas, in different slots of one plan.
-// The chunk of such an expert is read once, by the workgroup of its lowest
-// spare slot, and stored into every slot that holds it (the other slots'
-// workgroups return at once), so the stream moves (distinct experts + used
-// slots) x bytes_per_expert instead of 2 x used slots.  Workgroups are
-// numbered chunk-major, each chunk's slots rotated by the chunk index: the
-// workgroups resident at one time copy the same chunk of many slots (many
-// distant streams) and every slot's chunks spread over all XCDs (the
-// hardware hands consecutive workgroups to the 8 XCDs in turn), so empty
-// slots leave no XCD idle.  Up to kDedupMaxSpare spare slots; beyond that,
-// slot-major order without sharing.
+// A hot expert often has several replicas in one plan.  Each distinct expert
+// is read once and stored into every slot that holds it, so the stream moves
+// (distinct experts + filled slots) x bytes_per_expert instead of 2 x filled
+// slots.
+//
+// With a workspace (up to kListMaxSpare spare slots) the fill runs in two
+// launches:
+//   fill_list_kernel  one workgroup: the plan's fill list, i.e. the distinct
+//                     experts among the spare slots in order of their lowest
+//                     slot ("items"), and for each item the ordinals of the
+//                     slots that hold it, in ascending order;
+//   fill_copy_kernel  4 KiB per workgroup (one 16-byte vector per thread),
+//                     each chunk of an item read once and stored into every
+//                     slot of the item; the workgroups of one item stream
+//                     128 KiB of its weights in address order before the next
+//                     item's run (see the kernel for the numbering).
+// Small workgroups that each move one 16-byte vector per thread keep the most
+// bytes in flight; reading an item's rows in address order lets the memory
+// stream them.  Without a workspace, or with more spare slots, each workgroup
+// finds its slot's expert and the other holders itself
+// (slot_fill_shared_kernel, 16 KiB chunks), or above kDedupMaxSpare spare slots
+// copies its own slot (slot_fill_kernel).
 #include "ep_internal.h"
 
 namespace ep {
 namespace {
 
-#ifndef EP_FILL_THREADS
-#define EP_FILL_THREADS 256
-#endif
-#ifndef EP_FILL_UNROLL
-#define EP_FILL_UNROLL 4
-#endif
-#ifndef EP_FILL_CHUNK_ITERS
-#define EP_FILL_CHUNK_ITERS 1
-#endif
-#ifndef EP_FILL_SHARED
-#define EP_FILL_SHARED 1
-#endif
-constexpr int kFillThreads = EP_FILL_THREADS;
-constexpr int kFillUnroll = EP_FILL_UNROLL;
-constexpr int64_t kFillChunk = (int64_t)kFillThreads * kFillUnroll * EP_FILL_CHUNK_ITERS;  // 16-byte vectors
+constexpr int kFillThreads = 256;
+constexpr int kFillUnroll = 4;
+constexpr int64_t kFillChunk = (int64_t)kFillThreads * kFillUnroll;  // 16-byte vectors
+constexpr int kListMaxSpare = 1024;
+constexpr int kDedupMaxSpare = 1024;
+constexpr uint32_t kSuperChunks = 32;  // 4 KiB chunks an item streams before the next item
 
 // Weights are loaded through the caches; slot rows are stored as streaming
-// (nontemporal) writes: nothing in this launch reads them back, and keeping them
-// out of L2 measured 1 to 2% faster per layer on every workload.
+// (nontemporal) writes: nothing in this launch reads them back.
 #define LD(p) (*(p))
 #define ST(v, p) __builtin_nontemporal_store(v, p)
 
+// ----------------------------------------------------------------- fill list
+// ws layout (int32), n = number of items:
+//   [0]                  n
+//   [1, 1 + S)           the item's expert, items in order of their lowest slot
+//   [1 + S, 2 + S + n)   the item's first target (and the total after the last)
+//   [2 + 2S, 2 + 3S)     the targets: spare ordinals grouped by item, ascending
+// A copy workgroup reads n, its item's expert and its two target bounds
+// (scalar loads; the words are shared by many workgroups).
+__global__ __launch_bounds__(kListMaxSpare) void fill_list_kernel(const int32_t *__restrict__ phy2log,
+                                                                 const int32_t *__restrict__ spare_slot,
+                                                                 int32_t S, int32_t E,
+                                                                 int32_t *__restrict__ ws) {
+    __shared__ int32_t key[kListMaxSpare];
+    __shared__ int32_t first[kListMaxSpare];  // first target of a leader's item
+    __shared__ int32_t scan[kListMaxSpare];
+    const int o = threadIdx.x;
+    int e = -1;
+    if (o < S) {
+        e = phy2log[spare_slot[o]];
+        if (e < 0 || e >= E) e = -1;
+        key[o] = e;
+    }
+    __syncthreads();
+    // lowest ordinal holding the same expert, this ordinal's rank among the
+    // holders, and (for the lowest) the number of holders
+    int lead = o, rank = 0, holders = 0;
+    if (o < S && e >= 0) {
+        lead = -1;
+        for (int i = 0; i < S; i++) {
+            const bool same = key[i] == e;
+            if (same && lead < 0) lead = i;
+            rank += (same && i < o) ? 1 : 0;
+            holders += same ? 1 : 0;
+        }
+    }
+    const bool is_lead = o < S && e >= 0 && lead == o;
+    // inclusive scan over the leaders (item count in the high half) and their
+    // holder counts (targets in the low half), in ordinal order
+    const int mine = is_lead ? (1 << 16) | holders : 0;  // counts < 2^16 (S <= 1024)
+    scan[o] = mine;
+    __syncthreads();
+    for (int d = 1; d < kListMaxSpare; d <<= 1) {
+        const int v = o >= d ? scan[o - d] : 0;
+        __syncthreads();
+        scan[o] += v;
+        __syncthreads();
+    }
+    if (is_lead) {
+        const int excl = scan[o] - mine;
+        first[o] = excl & 0xffff;
+        ws[1 + (excl >> 16)] = e;
+        ws[1 + S + (excl >> 16)] = excl & 0xffff;
+    }
+    if (o == kListMaxSpare - 1) {
+        const int total = scan[o];
+        ws[0] = total >> 16;
+        ws[1 + S + (total >> 16)] = total & 0xffff;
+    }
+    __syncthreads();
+    if (o < S && e >= 0) ws[2 + 2 * S + first[lead] + rank] = o;
+}
+
+// Workgroup b copies chunk c of item i: in super-chunks of M chunks
+// (M = min(kSuperChunks, chunks per expert)), item-major inside each,
+// b -> (super-chunk, item, chunk).  An item's workgroups thus stream M
+// consecutive chunks (up to 128 KiB) of its expert before the next item's run
+// starts, and the workgroups of item numbers past the plan's last item (which
+// return at once) are spread over the whole launch instead of all dispatched
+// at its end.
+__global__ __launch_bounds__(kFillThreads) void fill_copy_kernel(const u32x4 *__restrict__ w, int64_t vpe,
+                                                                int64_t nch, int32_t S, uint32_t M,
+                                                                const int32_t *__restrict__ ws,
+                                                                u32x4 *__restrict__ buf) {
+    // (the grid has fewer than 2^31 workgroups: 32-bit index arithmetic)
+    const uint32_t b = blockIdx.x;
+    const uint32_t per = (uint32_t)S * M;
+    const uint32_t sc = b / per, r = b - sc * per;
+    const int item = (int)(r / M);
+    const int64_t c = (int64_t)sc * M + (r - (uint32_t)item * M);
+    if (item >= ws[0] || c >= nch) return;
+    const int e = ws[1 + item];
+    const int t0 = ws[1 + S + item], t1 = ws[2 + S + item];
+    const int32_t *tg = ws + 2 + 2 * S;
+    const int64_t i = c * kFillThreads + threadIdx.x;
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (i < vpe) x = LD(w + (int64_t)e * vpe + i);
+    for (int t = t0; t < t1; t++)
+        if (i < vpe) ST(x, buf + (int64_t)tg[t] * vpe + i);
+}
+
+// ------------------------------------------------ without a fill list
 __global__ __launch_bounds__(kFillThreads) void slot_fill_kernel(
     const u32x4 *__restrict__ w, int64_t vpe, int32_t E, const int32_t *__restrict__ phy2log,
     const int32_t *__restrict__ spare_slot, u32x4 *__restrict__ buf) {
@@ -64,9 +155,10 @@ __global__ __launch_bounds__(kFillThreads) void slot_fill_kernel(
     for (; i < c1; i += kFillThreads) ST(LD(src + i), dst + i);
 }
 
-constexpr int kDedupMaxSpare = 1024;
-static_assert(EP_FILL_CHUNK_ITERS == 1, "a shared-fill workgroup holds its whole chunk in registers");
-
+// Workgroups are numbered chunk-major, each chunk's slots rotated by the chunk
+// index, so the slots' chunks spread over all XCDs; the workgroup of the
+// lowest slot holding an expert loads the chunk and stores it into every slot
+// that holds the expert, the others return after that check.
 __global__ __launch_bounds__(kFillThreads) void slot_fill_shared_kernel(
     const u32x4 *__restrict__ w, int64_t vpe, int32_t E, const int32_t *__restrict__ phy2log,
     const int32_t *__restrict__ spare_slot, int32_t S, u32x4 *__restrict__ buf) {
@@ -77,7 +169,6 @@ __global__ __launch_bounds__(kFillThreads) void slot_fill_shared_kernel(
     const int e = phy2log[spare_slot[o]];
     if (e < 0 || e >= E) return;
     const int lane = threadIdx.x % kWave;
-    // the lowest spare slot holding e does the work
     for (int base = 0; base < o; base += kWave) {
         const int j = base + lane;
         const bool hit = j < o && phy2log[spare_slot[j]] == e;
@@ -93,8 +184,6 @@ __global__ __launch_bounds__(kFillThreads) void slot_fill_shared_kernel(
         const int64_t i = i0 + u * kFillThreads;
         if (i < c1) x[u] = LD(src + i);
     }
-    // store into every slot holding e, from o on (the slot list is read while
-    // the chunk loads)
     for (int base = o; base < S; base += kWave) {
         const int j = base + lane;
         for (uint64_t m = __ballot(j < S && phy2log[spare_slot[j]] == e); m; m &= m - 1) {
@@ -110,15 +199,31 @@ __global__ __launch_bounds__(kFillThreads) void slot_fill_shared_kernel(
 
 }  // namespace
 
+size_t fill_ws_bytes(int32_t S) {
+    return S <= 0 || S > kListMaxSpare ? 0 : (3 * (size_t)S + 2) * sizeof(int32_t);
+}
+
 hipError_t launch_slot_fill(const void *w, int64_t bytes_per_expert, const int32_t *phy2log,
-                            const ep_layout_t &L, void *buf, hipStream_t s) {
-    if (L.num_spare == 0) return hipSuccess;
+                            const ep_layout_t &L, void *buf, int32_t *ws, hipStream_t s) {
+    const int S = L.num_spare;
+    if (S == 0) return hipSuccess;
     const int64_t vpe = bytes_per_expert / 16;
-    dim3 grid((unsigned)((vpe + kFillChunk - 1) / kFillChunk), (unsigned)L.num_spare);
-    if (L.num_spare <= kDedupMaxSpare && EP_FILL_SHARED) {
+    const int64_t nch = (vpe + kFillThreads - 1) / kFillThreads;
+    const uint32_t M = nch < (int64_t)kSuperChunks ? (uint32_t)nch : kSuperChunks;
+    const int64_t ncopy = (nch + M - 1) / M * M * S;
+    if (ws && S <= kListMaxSpare && ncopy <= 0x7fffffffLL) {
+        hipLaunchKernelGGL(fill_list_kernel, dim3(1), dim3(kListMaxSpare), 0, s, phy2log,
+                           tables_of(L).spare_slot, S, L.num_experts, ws);
+        hipLaunchKernelGGL(fill_copy_kernel, dim3((unsigned)ncopy), dim3(kFillThreads), 0, s,
+                           reinterpret_cast<const u32x4 *>(w), vpe, nch, S, M, ws,
+                           reinterpret_cast<u32x4 *>(buf));
+        return hipGetLastError();
+    }
+    dim3 grid((unsigned)((vpe + kFillChunk - 1) / kFillChunk), (unsigned)S);
+    if (S <= kDedupMaxSpare) {
         hipLaunchKernelGGL(slot_fill_shared_kernel, grid, dim3(kFillThreads), 0, s,
                            reinterpret_cast<const u32x4 *>(w), vpe, L.num_experts, phy2log,
-                           tables_of(L).spare_slot, L.num_spare, reinterpret_cast<u32x4 *>(buf));
+                           tables_of(L).spare_slot, S, reinterpret_cast<u32x4 *>(buf));
     } else {
         hipLaunchKernelGGL(slot_fill_kernel, grid, dim3(kFillThreads), 0, s,
                            reinterpret_cast<const u32x4 *>(w), vpe, L.num_experts, phy2log,

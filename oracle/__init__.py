@@ -41,7 +41,8 @@ def lib() -> ctypes.CDLL:
                                  ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
         _lib.or_plan.restype = ctypes.c_int
         _lib.or_plan_domain.argtypes = [i32, i32, i32p, i32p, i32p, i32p, i32p, i32p, i32p, i32p, i32, i32,
-                                        ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
+                                        ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32),
+                                        ctypes.POINTER(ctypes.c_int32)]
         _lib.or_plan_domain.restype = ctypes.c_int
         _lib.or_reroute.argtypes = [i32p, i64, i32, i32p, i32p, i32p, i32, i32p]
         _lib.or_reroute.restype = ctypes.c_int64
@@ -128,6 +129,7 @@ class Plan:
     log2phy: np.ndarray     # [E][rho]
     steps: int
     cap_hit: int
+    bad_load: int = 0       # a load < 0 or a total above INT32_MAX: no move was made
 
 
 def plan(load: np.ndarray, layout: Layout, ranks_per_domain: int = 0) -> Plan:
@@ -141,11 +143,13 @@ def plan(load: np.ndarray, layout: Layout, ranks_per_domain: int = 0) -> Plan:
     log2phy = np.zeros(E * rho, np.int32)
     steps = ctypes.c_int32(0)
     cap = ctypes.c_int32(0)
+    bad = ctypes.c_int32(0)
     rc = lib().or_plan_domain(*layout.args(), load, phy2log, quota, logcnt, log2phy, rho,
-                              int(ranks_per_domain), ctypes.byref(steps), ctypes.byref(cap))
+                              int(ranks_per_domain), ctypes.byref(steps), ctypes.byref(cap), ctypes.byref(bad))
     if rc != 0:
         raise ValueError(f"oracle: bad layout ({rc})")
-    return Plan(phy2log, quota, logcnt, log2phy.reshape(E, rho), int(steps.value), int(cap.value))
+    return Plan(phy2log, quota, logcnt, log2phy.reshape(E, rho), int(steps.value), int(cap.value),
+                int(bad.value))
 
 
 def reroute(ids: np.ndarray, num_experts: int, phy_quota, log2phy, logcnt):

@@ -188,10 +188,14 @@ typedef struct { int slot; int expert; int64_t quota; } cand_t;
  * expert's native rank (rank r lies in domain r / D) [UltraEP article, section
  * on why it reaches the optimum: hot-expert replication stays inside the
  * high-bandwidth scale-up domain]; D = 0 places replicas anywhere. */
+/* Loads must be >= 0 with a total that fits int32 (the widths of the tables);
+ * a plan that breaks this makes no move and keeps the native placement, and
+ * *bad_load_out is set. */
 int or_plan_domain(int32_t E, int32_t R, const int32_t *native_count, const int32_t *native_experts,
                    const int32_t *spare_count, const int32_t *load,
                    int32_t *phy2log, int32_t *phy_quota, int32_t *logcnt, int32_t *log2phy,
-                   int32_t rho, int32_t ranks_per_domain, int32_t *steps_out, int32_t *cap_hit_out) {
+                   int32_t rho, int32_t ranks_per_domain, int32_t *steps_out, int32_t *cap_hit_out,
+                   int32_t *bad_load_out) {
     layout_t L;
     int rc = layout_build(&L, E, R, native_count, native_experts, spare_count);
     if (rc != OR_OK) return rc;
@@ -216,9 +220,17 @@ int or_plan_domain(int32_t E, int32_t R, const int32_t *native_count, const int3
     }
     for (int r = 0; r < R; r++) freec[r] = L.spare_cnt[r];
 
+    int64_t total = 0;
+    int bad_load = 0;
+    for (int e = 0; e < E; e++) {
+        if (load[e] < 0) bad_load = 1;
+        total += load[e];
+    }
+    if (total > INT32_MAX) bad_load = 1;
+
     const int cap = 2 * L.S + R;
     int steps = 0, cap_hit = 0;
-    for (;;) {
+    while (!bad_load) {
         if (steps == cap) { cap_hit = 1; break; }
         /* hottest rank, lowest index on ties */
         int h = 0;
@@ -308,6 +320,7 @@ int or_plan_domain(int32_t E, int32_t R, const int32_t *native_count, const int3
     }
     if (steps_out) *steps_out = steps;
     if (cap_hit_out) *cap_hit_out = cap_hit;
+    if (bad_load_out) *bad_load_out = bad_load;
 
     free(owner); free(quota); free(rl); free(freec); free(cand);
     free(ir); free(is); free(ib); free(iq); free(nq);
@@ -320,7 +333,7 @@ int or_plan(int32_t E, int32_t R, const int32_t *native_count, const int32_t *na
             int32_t *phy2log, int32_t *phy_quota, int32_t *logcnt, int32_t *log2phy,
             int32_t rho, int32_t *steps_out, int32_t *cap_hit_out) {
     return or_plan_domain(E, R, native_count, native_experts, spare_count, load, phy2log, phy_quota,
-                          logcnt, log2phy, rho, 0, steps_out, cap_hit_out);
+                          logcnt, log2phy, rho, 0, steps_out, cap_hit_out, NULL);
 }
 
 /* ------------------------------------------------------------------------- */

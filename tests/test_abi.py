@@ -20,6 +20,7 @@ def _declared():
 def test_header_declares_the_path():
     names = _declared()
     for n in ("ep_load_histogram", "ep_plan_quota", "ep_reroute", "ep_slot_fill", "ep_balance_stats",
+              "ep_slot_fill_workspace_bytes", "ep_sub_block_pairs",
               "ep_workspace_bytes", "ep_layout_init", "ep_layout_table_ints", "ep_status_string",
               "ep_dispatch_layout", "ep_replica_grad_reduce", "ep_route_noalloc"):
         assert n in names
@@ -69,7 +70,17 @@ def test_host_side_checks_without_gpu():
     # slot fill needs a multiple of 16 bytes per expert
     lay_ok = ep._CLayout(12, 8, 16, 4, 5, 2, 1, 0, ctypes.c_void_p(16))
     rc = L.ep_slot_fill(ctypes.c_void_p(16), 24, ctypes.c_void_p(16), ctypes.byref(lay_ok),
-                        ctypes.c_void_p(16), None)
+                        ctypes.c_void_p(16), None, 0, None)
+    assert rc == ep.EP_ERR_INVALID_ARG
+    # its optional fill-list workspace: 3 int32 values per spare slot (item
+    # expert, item start, target) and two more (item count, end of the last
+    # item); a smaller or misaligned one is rejected
+    assert L.ep_slot_fill_workspace_bytes(ctypes.byref(lay_ok)) == (3 * 4 + 2) * 4
+    rc = L.ep_slot_fill(ctypes.c_void_p(16), 32, ctypes.c_void_p(16), ctypes.byref(lay_ok),
+                        ctypes.c_void_p(16), ctypes.c_void_p(64), 55, None)
+    assert rc == ep.EP_ERR_INVALID_ARG
+    rc = L.ep_slot_fill(ctypes.c_void_p(16), 32, ctypes.c_void_p(16), ctypes.byref(lay_ok),
+                        ctypes.c_void_p(16), ctypes.c_void_p(72), 56, None)
     assert rc == ep.EP_ERR_INVALID_ARG
 
 
@@ -119,10 +130,9 @@ def test_entry_points_reject_unsupported_shapes_on_host():
     assert rc == ep.EP_ERR_INVALID_ARG
 
 
-def test_bench_sub_block_rule_matches_the_library():
-    # bench.py counts the histogram's count rows with its own copy of the
-    # sub-block rule; the library's workspace size pins it
-    import bench
+def test_sub_block_query_matches_the_workspace():
+    # ep_sub_block_pairs (which the bench uses to count the histogram's count
+    # rows) and ep_workspace_bytes agree on the geometry
     import moe_expert_load_layer_amd as ep
     if not os.path.exists(ep.LIB_PATH):
         pytest.skip("library not built")
@@ -130,7 +140,8 @@ def test_bench_sub_block_rule_matches_the_library():
     for N, P, E in [(4194304, 256, 384), (4194304, 94, 300), (100003, 3, 257), (1 << 20, 1, 300),
                     (5, 2, 1000), (4194304, 94, 128), (2097152, 58, 256), (5242880, 92, 160),
                     (4194304, 47, 128), (1000, 1, 12)]:
-        sub = bench._sub_pairs(N, P, E)
+        sub = ep.ep_sub_block_pairs(N, P, E)
+        assert sub >= 1024 and sub & (sub - 1) == 0
         nsb = -(-N // sub)
         nseg = -(-nsb // 8)
         rows = P * (nsb + nseg + 1) * (E + 1) * 4
@@ -154,3 +165,52 @@ def test_noalloc_host_checks_without_gpu():
     assert L.ep_route_noalloc(None, -1, 1, ctypes.byref(lay), *nul, None) == ep.EP_ERR_INVALID_ARG
     assert L.ep_route_noalloc(None, N, 70000, ctypes.byref(lay), *nul, None) == ep.EP_ERR_INVALID_ARG
 
+
+def test_sub_block_geometry():
+    # the sub-block sizes the launches use: about 8192 waves per launch, at
+    # least 8 (E + 1) pairs with E <= 256 and 16 (E + 1) above, 1024..4096
+    # unless that bound asks for more
+    import moe_expert_load_layer_amd as ep
+    if not os.path.exists(ep.LIB_PATH):
+        pytest.skip("library not built")
+    assert ep.ep_sub_block_pairs(4194304, 94, 128) == 4096     # 94 Qwen3-like plans
+    assert ep.ep_sub_block_pairs(4194304, 1, 128) == 2048      # one such plan
+    assert ep.ep_sub_block_pairs(2097152, 58, 256) == 4096     # DeepSeek-V3-like batch
+    assert ep.ep_sub_block_pairs(4194304, 256, 384) == 8192    # stress batch
+    assert ep.ep_sub_block_pairs(512, 2, 12) == 1024
+    assert ep.ep_sub_block_pairs(-1, 1, 12) == 0
+    # the count rows: one row of E + 1 int32 per sub-block, plus segment rows
+    N, P, E = 4194304, 94, 128
+    sub = ep.ep_sub_block_pairs(N, P, E)
+    nsb = -(-N // sub)
+    nseg = -(-nsb // 8)
+    rows = P * (nsb + nseg + 1) * (E + 1) * 4
+    assert ep.ep_workspace_bytes(N, P, E) >= rows + P * N
+
+
+def test_pipelined_route_host_checks_without_gpu():
+    # the overlapped chain refuses bad chunkings and stream sets on the host,
+    # before any HIP call
+    import moe_expert_load_layer_amd as ep
+    if not os.path.exists(ep.LIB_PATH):
+        pytest.skip("library not built")
+    L = ep.lib()
+    i32 = ctypes.c_int32
+    sizes = (i32 * 2)(3, 4)
+    E, N = 12, 1000
+    one = L.ep_workspace_bytes(N, 3, E)
+    two = L.ep_workspace_bytes(N, 4, E)
+    r256 = lambda x: (x + 255) // 256 * 256
+    assert L.ep_pipeline_workspace_bytes(N, sizes, 2, E) == r256(one) + r256(two)
+    assert L.ep_pipeline_workspace_bytes(N, sizes, 17, E) == 0          # more than EP_MAX_CHUNKS
+    lay = ep._CLayout(12, 8, 16, 4, 5, 2, 1, 0, ctypes.c_void_p(16))
+    fake = ctypes.c_void_p(4096)
+    ev = (ctypes.c_void_p * 6)(*([4096] * 6))
+    args = lambda P, ch, n, s0, s1, s2: L.ep_route_pipelined(
+        fake, N, P, ctypes.byref(lay), ch, n, fake, fake, fake, fake, fake, fake, None, fake, fake, 1 << 20,
+        s0, s1, s2, ev)
+    s_a, s_b = ctypes.c_void_p(8), ctypes.c_void_p(24)
+    assert args(8, sizes, 2, None, s_a, s_b) == ep.EP_ERR_INVALID_ARG      # chunks sum to 7, not 8
+    assert args(7, sizes, 2, None, s_a, s_a) == ep.EP_ERR_INVALID_ARG      # one side stream twice
+    assert args(7, sizes, 2, s_a, s_a, s_b) == ep.EP_ERR_INVALID_ARG       # side stream = caller's
+    assert args(7, sizes, 0, None, s_a, s_b) == ep.EP_ERR_INVALID_ARG      # no chunk

@@ -76,6 +76,36 @@ def test_dispatch_edges(dev, N):
     _check(ids_h, E, plans, off, pos, src)
 
 
+@pytest.mark.parametrize("N", [40, 5000])
+def test_dispatch_over_quota_plan(dev, N):
+    # quotas above the loads: an instance in the middle of an expert's list and
+    # the last instance of another get extra units, so positions inside the
+    # layout (not only past its end) are taken by no pair and must hold -1
+    rng = np.random.default_rng(77 + N)
+    E, R = 10, 4
+    nc, ne, sc = [3, 3, 2, 2], list(range(E)), [2, 2, 1, 1]
+    lay_o = oracle.Layout.of(E, R, nc, ne, sc)
+    ids = torch.from_numpy(rng.choice(3, size=(1, N), p=[0.6, 0.3, 0.1]).astype(np.int32))
+    ids_h = ids.numpy()
+    pl = oracle.plan(oracle.histogram(ids_h[0], E)[0], lay_o)
+    multi = [e for e in range(E) if pl.logcnt[e] >= 2]
+    assert multi, "the skewed load should replicate an expert"
+    e0 = multi[0]
+    pl.phy_quota[pl.log2phy[e0, 0]] += 5          # a gap before e0's second instance
+    pl.phy_quota[pl.log2phy[1, pl.logcnt[1] - 1]] += 3
+    ro, rp, rs, placed = oracle.dispatch(ids_h[0], E, pl.phy_quota, pl.log2phy, pl.logcnt)
+    assert placed == N and np.any((rs[:-1] == -1) & (rs[1:] >= 0))   # a gap inside the layout
+    lay = ep.Layout.create(E, nc, ne, sc, device=dev)
+    d = ids.to(dev)
+    _, ws, _ = ep.ep_load_histogram(d, lay)
+    st = lambda k: torch.from_numpy(getattr(pl, k)[None].copy()).to(dev)
+    src_junk = torch.full((1, N), 12345, dtype=torch.int32, device=dev)
+    off, pos, src = ep.ep_dispatch_layout(d, lay, st("phy_quota"), st("log2phy"), st("logcnt"), ws,
+                                          dispatch_src=src_junk)
+    torch.cuda.synchronize()
+    _check(ids_h, E, [pl], off, pos, src)
+
+
 @pytest.mark.parametrize("name", W.WORKLOAD_ORDER)
 def test_dispatch_fullsize_chain(dev, name):
     wl = W.get(name)

@@ -40,10 +40,14 @@ def _ids(E, P, N, seed):
     return out
 
 
-@pytest.mark.parametrize("E,R,S", [(1500, 100, 63), (1024, 1024, 63), (1200, 64, 63)])
+@pytest.mark.parametrize("E,R,S", [(1500, 100, 63), (1024, 1024, 63), (1200, 64, 63), (2048, 2048, 63),
+                                   (3000, 200, 63)])
 def test_large_layouts_full_chain(dev, E, R, S):
-    # (1500, 100) and (1024, 1024): the generic planner near its LDS limit;
-    # (1200, 64): 19 natives per rank, also the generic planner
+    # (1500, 100) and (1024, 1024): the generic planner with a 64 KiB table;
+    # (1200, 64): 19 natives per rank, also the generic planner; (2048, 2048)
+    # and (3000, 200): tables of 122 KiB and 123 KiB, beyond 64 KiB of LDS
+    # (gfx950 gives a workgroup up to 160 KiB), with the reroute and the
+    # dispatch layout at 2048 and 3000 experts
     nc, ne, sc = _layout(E, R, S, E + R)
     P, N = 2, 300_007
     ids_h = _ids(E, P, N, E * 7 + R)
@@ -71,10 +75,11 @@ def test_large_layouts_full_chain(dev, E, R, S):
 
 
 def test_largest_histogram_and_reroute(dev):
-    # E = 2047 fills the histogram's LDS exactly (8 waves x 2048 counters); 32
-    # natives per rank are beyond both planner kernels, so the planner must
+    # E = 5119 fills the histogram's 160 KiB of LDS exactly (8 waves x 5120
+    # counters); 80 natives per rank are beyond both planner kernels (the
+    # generic planner's tables would take 203 KiB), so the planner must
     # refuse and the reroute runs on the oracle's plan
-    E, R, S = 2047, 64, 64
+    E, R, S = 5119, 64, 64
     nc, ne, sc = _layout(E, R, S, 9)
     P, N = 2, 400_003
     ids_h = _ids(E, P, N, 11)

@@ -192,6 +192,31 @@ def test_plan_step_cap_binds(dev, kernel):
         assert int(st[p]) == 0x40 | (ep.EP_STATUS_STEP_CAP if r.cap_hit else 0)
 
 
+@pytest.mark.parametrize("kernel", sorted(_CAP_CASES))
+def test_plan_loads_outside_int32(dev, kernel):
+    # plans whose loads hold a negative value or sum past INT32_MAX make no
+    # move and are flagged; a plan whose total is exactly INT32_MAX is planned
+    E, nc, ne, sc, hot = _CAP_CASES[kernel]
+    lay_o = oracle.Layout.of(E, 3, nc, ne, sc)
+    rows = [hot, [37, -1, 34], [2**31 - 1, 1, 0], [2**30, 2**30, 0], [2**31 - 1 - 10, 10, 0]]
+    loads = np.zeros((len(rows), E), np.int64)
+    for i, r in enumerate(rows):
+        loads[i, :len(r)] = r
+    loads = loads.astype(np.int32)
+    refs = [oracle.plan(l, lay_o) for l in loads]
+    assert [r.bad_load for r in refs] == [0, 1, 1, 1, 0]
+    print(f"[plan bad loads] {kernel} E={E}", flush=True)
+    lay = ep.Layout.create(E, nc, ne, sc, device=dev)
+    status = torch.zeros((len(rows),), dtype=torch.int32, device=dev)
+    out = ep.ep_plan_quota(torch.from_numpy(loads).to(dev), lay, status=status)
+    torch.cuda.synchronize()
+    _assert_plan_equal(out, refs)
+    st = _np(status)
+    for p, r in enumerate(refs):
+        want = (ep.EP_STATUS_STEP_CAP if r.cap_hit else 0) | (ep.EP_STATUS_BAD_LOAD if r.bad_load else 0)
+        assert int(st[p]) == want, p
+
+
 # --------------------------------------------------------------------- A3
 @pytest.mark.parametrize("name", W.WORKLOAD_ORDER)
 def test_reroute_with_oracle_plan(dev, name):
@@ -281,11 +306,13 @@ def test_slot_fill_with_oracle_plan(dev, name):
         np.testing.assert_array_equal(_np(buf.view(torch.int16)), ref)
 
 
+@pytest.mark.parametrize("use_ws", [True, False])
 @pytest.mark.parametrize("S", [8, 300, 1024, 1025])
-def test_slot_fill_replicated_experts(dev, S):
+def test_slot_fill_replicated_experts(dev, S, use_ws):
     # a few experts fill most spare slots (each read once for all its slots
     # up to 1024 spare slots, slot by slot above), some slots empty; rows of
-    # two whole 16 KiB chunks and a tail
+    # two whole 16 KiB chunks and a tail; with the fill-list workspace and
+    # without it
     E, R = 16, 16
     nc, ne = [1] * R, list(range(E))
     sc = [S // R + (1 if r < S % R else 0) for r in range(R)]
@@ -300,13 +327,55 @@ def test_slot_fill_replicated_experts(dev, S):
     ref = np.full((S, elems), 0x7FC1, np.uint16)
     oracle.slot_fill(w, phy2log, lay_o, ref)
     buf = torch.from_numpy(np.full((S, elems), 0x7FC1, np.uint16).view(np.int16)).to(dev)
-    ep.ep_slot_fill(torch.from_numpy(w.view(np.int16)).to(dev), torch.from_numpy(phy2log).to(dev), lay, buf)
+    ep.ep_slot_fill(torch.from_numpy(w.view(np.int16)).to(dev), torch.from_numpy(phy2log).to(dev), lay, buf,
+                    use_ws=use_ws)
     torch.cuda.synchronize()
     assert np.array_equal(buf.cpu().numpy().view(np.uint16), ref)
 
 
+@pytest.mark.parametrize("case", ["one_slot", "one_expert_everywhere", "all_empty", "one_vector",
+                                  "ws_reused"])
+def test_slot_fill_list_edges(dev, case):
+    # the fill list at its edges: a single spare slot, one expert in every
+    # slot (64 stores per chunk), no expert at all, 16-byte experts (one
+    # vector, one partial workgroup), and one workspace reused by plans with
+    # fewer and more distinct experts than the last
+    E, R = 64, 64
+    nc, ne = [1] * R, list(range(E))
+    sc = [1 if (case != "one_slot" or r == 5) else 0 for r in range(R)]
+    lay = ep.Layout.create(E, nc, ne, sc, device=dev)
+    lay_o = oracle.Layout.of(E, R, nc, ne, sc)
+    first, home, rank, spare = lay_o.slots()
+    S = len(spare)
+    rng = np.random.default_rng(21)
+    elems = 8 if case == "one_vector" else 2048 * 3 + 8
+    w = rng.integers(0, 1 << 16, size=(E, elems), dtype=np.uint16)
+    d_w = torch.from_numpy(w.view(np.int16)).to(dev)
+    ws = ep.slot_fill_workspace(lay, dev)
+    ws.fill_(0x55)
+    plans = []
+    if case == "one_expert_everywhere":
+        plans.append(np.full(S, 7))
+    elif case == "all_empty":
+        plans.append(np.full(S, -1))
+    elif case == "ws_reused":
+        plans += [rng.integers(-1, 4, size=S), rng.integers(-1, E, size=S), np.full(S, 3), rng.integers(-1, 2, size=S)]
+    else:
+        plans.append(rng.integers(0, E, size=S))
+    for sp in plans:
+        phy2log = home.astype(np.int32).copy()
+        phy2log[spare] = sp
+        ref = np.full((S, elems), 0x7FC1, np.uint16)
+        oracle.slot_fill(w, phy2log, lay_o, ref)
+        buf = torch.from_numpy(np.full((S, elems), 0x7FC1, np.uint16).view(np.int16)).to(dev)
+        ep.ep_slot_fill(d_w, torch.from_numpy(phy2log).to(dev), lay, buf, ws=ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(buf.cpu().numpy().view(np.uint16), ref)
+
+
+@pytest.mark.parametrize("use_ws", [True, False])
 @pytest.mark.parametrize("S", [8, 1025])
-def test_slot_fill_entries_naming_no_expert(dev, S):
+def test_slot_fill_entries_naming_no_expert(dev, S, use_ws):
     # spare entries outside [0, E) (E, E + 7, INT32_MAX) name no expert: their
     # rows keep the sentinel, in the shared fill (S <= 1024) and the per-slot one
     E, R = 16, 16
@@ -323,7 +392,8 @@ def test_slot_fill_entries_naming_no_expert(dev, S):
     ref = np.full((S, elems), 0x7FC1, np.uint16)
     oracle.slot_fill(w, phy2log, lay_o, ref)
     buf = torch.from_numpy(np.full((S, elems), 0x7FC1, np.uint16).view(np.int16)).to(dev)
-    ep.ep_slot_fill(torch.from_numpy(w.view(np.int16)).to(dev), torch.from_numpy(phy2log).to(dev), lay, buf)
+    ep.ep_slot_fill(torch.from_numpy(w.view(np.int16)).to(dev), torch.from_numpy(phy2log).to(dev), lay, buf,
+                    use_ws=use_ws)
     torch.cuda.synchronize()
     assert np.array_equal(buf.cpu().numpy().view(np.uint16), ref)
 

@@ -204,6 +204,25 @@ def test_plan_by_hand_step_cap_with_idle_natives():
     assert (pl.steps, pl.cap_hit) == (9, 1)
 
 
+def test_plan_rejects_loads_outside_int32():
+    # loads are counts: >= 0, and quotas and rank loads are int32 partial sums
+    # of them, so a plan whose loads include a negative value or whose total
+    # passes INT32_MAX makes no move: native placement, quota = load, flagged
+    lay = oracle.Layout.of(3, 3, [1, 1, 1], [0, 1, 2], [1, 2, 0])
+    _, home, _, _ = lay.slots()
+    for load in ([37, -1, 34], [2**31 - 1, 1, 0], [2**30, 2**30, 0]):
+        pl = oracle.plan(np.array(load, np.int64), lay)
+        assert (pl.steps, pl.cap_hit, pl.bad_load) == (0, 0, 1)
+        np.testing.assert_array_equal(pl.phy2log, home)
+        np.testing.assert_array_equal(pl.phy_quota[home >= 0], np.array(load)[home[home >= 0]])
+        assert pl.logcnt.tolist() == [1, 1, 1]
+    # a total of exactly INT32_MAX is planned as usual
+    load = np.array([2**31 - 1 - 10, 10, 0], np.int64)
+    pl = oracle.plan(load, lay)
+    assert pl.bad_load == 0 and pl.steps > 0
+    check_plan_invariants(load, lay, pl)
+
+
 # ------------------------------------------------------------ invariants
 def check_plan_invariants(load, lay, pl):
     E, Phi = lay.num_experts, lay.num_phys
