@@ -150,7 +150,7 @@ int64_t ep_sub_block_pairs(int64_t pairs_per_plan, int32_t num_plans, int32_t nu
  *   ws        device, >= ep_workspace_bytes(N, P, E) bytes, 16-byte aligned
  *   status    device uint32 [P] (written: EP_STATUS_BAD_ID or 0)
  * N may be 0 (loads become 0).  Requires N < 2^31, 1 <= P <= 65535 and
- * E <= 2047 (eight LDS histograms of E + 1 counters in a workgroup).
+ * E <= 5119 (eight LDS histograms of E + 1 counters in a workgroup's 160 KiB).
  */
 int ep_load_histogram(const int32_t *topk_ids, int64_t pairs_per_plan, int32_t num_plans,
                       const ep_layout_t *layout, int32_t *load, void *ws, size_t ws_bytes,
@@ -189,8 +189,8 @@ int ep_load_histogram(const int32_t *topk_ids, int64_t pairs_per_plan, int32_t n
  * it keeps the native placement (quota = load) and gets EP_STATUS_BAD_LOAD.
  * Requires rho <= 64 (at most 64 instances of one expert), 1 <= P <= 65535,
  * and either R <= 64 with at most 8 natives and 16 spare slots per rank, or
- * tables that fit the generic kernel's 64 KiB of LDS (about 60 bytes per rank
- * and per expert: R = E up to about 1050); other layouts return
+ * tables that fit the generic kernel's 160 KiB of LDS (about 60 bytes per rank
+ * and per expert: R = E up to about 2700); other layouts return
  * EP_ERR_INVALID_ARG.
  */
 int ep_plan_quota(const int32_t *load, int32_t num_plans, const ep_layout_t *layout,
@@ -215,8 +215,8 @@ int ep_plan_quota(const int32_t *load, int32_t num_plans, const ep_layout_t *lay
  *   phys_ids  device int32 [P][N] (written): physical slot, -1 for padding,
  *             invalid IDs and pairs beyond the expert's total quota
  * phys_ids 4-byte aligned.  LDS bounds the shape: 16 E + 8 Phi + 256 bytes
- * must fit 64 KiB (E = 2047 with Phi up to about 4000); otherwise, and for
- * a ws smaller than ep_workspace_bytes(N, P, E), EP_ERR_INVALID_ARG.
+ * must fit 160 KiB (E up to about 6800 at Phi = E); otherwise, and for a ws
+ * smaller than ep_workspace_bytes(N, P, E), EP_ERR_INVALID_ARG.
  */
 int ep_reroute(const int32_t *topk_ids, int64_t pairs_per_plan, int32_t num_plans,
                const ep_layout_t *layout, const int32_t *phy_quota, const int32_t *log2phy,
@@ -230,18 +230,22 @@ int ep_reroute(const int32_t *topk_ids, int64_t pairs_per_plan, int32_t num_plan
  * histogram of chunk c + 1 streams, and the reroute of chunk c while the
  * planner of chunk c + 1 runs.  The outputs are exactly those of
  * ep_load_histogram, ep_plan_quota and ep_reroute made in order on one stream
- * (arguments and layouts as there, P plans).
+ * (arguments and layouts as there, P plans).  Kernels of two streams run side
+ * by side only when the streams sit on different hardware queues; the HIP
+ * runtime spreads streams over its queues (GPU_MAX_HW_QUEUES of them, 4 by
+ * default) in creation order, so three streams created one after another get
+ * three queues, whereas a side stream that shares the queue of the caller's
+ * busy stream loses the overlap.
  *   chunk_plans  host int32 [num_chunks]: plans per chunk, each >= 1, summing
  *                to P; 1 <= num_chunks <= EP_MAX_CHUNKS
  *   ws           device, >= ep_pipeline_workspace_bytes(N, chunk_plans,
  *                num_chunks, E) bytes, 16-byte aligned: one histogram
  *                workspace per chunk
  *   stream       the caller's stream: the chain starts after the work already
- *                enqueued there and later work there waits for all of it;
- *                histograms run on it
- *   plan_stream, reroute_stream  two further streams of the caller (distinct
- *                from each other and from `stream`, default priority):
- *                planners and reroutes run on them
+ *                enqueued there and later work there waits for all of it
+ *   side_streams host array of three distinct streams of the caller, none of
+ *                them `stream`, default priority: histograms run on [0],
+ *                planners on [1], reroutes on [2]
  *   events       2 + 2 * num_chunks events of the caller (hipEvent_t, e.g.
  *                created with hipEventDisableTiming), recorded and waited on
  *                here; no other work may use them until the chain completes
@@ -255,8 +259,8 @@ int ep_route_pipelined(const int32_t *topk_ids, int64_t pairs_per_plan, int32_t 
                        const ep_layout_t *layout, const int32_t *chunk_plans, int32_t num_chunks,
                        int32_t *load, uint32_t *status, int32_t *phy2log, int32_t *phy_quota,
                        int32_t *logcnt, int32_t *log2phy, int32_t *steps, int32_t *phys_ids, void *ws,
-                       size_t ws_bytes, ep_stream_t stream, ep_stream_t plan_stream,
-                       ep_stream_t reroute_stream, void *const *events);
+                       size_t ws_bytes, ep_stream_t stream, const ep_stream_t *side_streams,
+                       void *const *events);
 
 /*
  * Next row after A3 -- dispatch layout for the token all-to-all (EPLB
@@ -274,7 +278,7 @@ int ep_route_pipelined(const int32_t *topk_ids, int64_t pairs_per_plan, int32_t 
  *   dispatch_src  device int32 [P][N] (written): pair index (within the plan)
  *                 at each position, -1 for positions no pair takes
  * All output arrays 4-byte aligned.  LDS bounds the shape: 24 E + 12 Phi + 20
- * bytes must fit 64 KiB (about E <= 1800 at Phi = E).
+ * bytes must fit 160 KiB (about E <= 4500 at Phi = E).
  */
 int ep_dispatch_layout(const int32_t *topk_ids, int64_t pairs_per_plan, int32_t num_plans,
                        const ep_layout_t *layout, const int32_t *phy_quota, const int32_t *log2phy,

@@ -78,7 +78,7 @@ def lib() -> ctypes.CDLL:
         L.ep_pipeline_workspace_bytes.argtypes = [i64, ctypes.POINTER(i32), i32, i32]
         L.ep_pipeline_workspace_bytes.restype = sz
         L.ep_route_pipelined.argtypes = [vp, i64, i32, lp, ctypes.POINTER(i32), i32, vp, vp, vp, vp, vp, vp, vp,
-                                         vp, vp, sz, vp, vp, vp, ctypes.POINTER(vp)]
+                                         vp, vp, sz, vp, ctypes.POINTER(vp), ctypes.POINTER(vp)]
         L.ep_status_string.argtypes = [ctypes.c_int]
         L.ep_status_string.restype = ctypes.c_char_p
         for f in ("ep_layout_init", "ep_load_histogram", "ep_plan_quota", "ep_reroute",
@@ -399,10 +399,12 @@ class PathPipeline:
     overlapped across three streams by the library's ep_route_pipelined: the
     planner of chunk c runs while the histogram of chunk c + 1 streams, and the
     reroute of chunk c while the planner of chunk c + 1 runs.  The outputs are
-    those of the same calls made in order on one stream.  Owns the two side
-    streams, the events and the per-chunk workspaces; the caller owns inputs and
-    outputs.  run() only enqueues: it is ordered after earlier work on the
-    caller's stream, and later work on that stream waits for it."""
+    those of the same calls made in order on one stream.  Owns the three side
+    streams (taken one after another from torch's pool, so that they sit on
+    three different hardware queues), the events and the per-chunk workspaces;
+    the caller owns inputs and outputs.  run() only enqueues: it is ordered
+    after earlier work on the caller's stream, and later work on that stream
+    waits for it."""
 
     def __init__(self, layout: Layout, num_plans: int, pairs_per_plan: int, chunks=2, device=None):
         """chunks: a number of equal chunks, or the list of chunk sizes (plans).
@@ -430,7 +432,9 @@ class PathPipeline:
         nbytes = lib().ep_pipeline_workspace_bytes(self.pairs_per_plan, self._sizes, len(sizes), layout.num_experts)
         self.ws = torch.empty(max(16, nbytes), dtype=torch.uint8, device=dev)
         # default-priority side streams; events created (by a first record) up front
-        self.s_plan, self.s_rr = torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev)
+        self.s_hist, self.s_plan, self.s_rr = (torch.cuda.Stream(device=dev) for _ in range(3))
+        self._side = (ctypes.c_void_p * 3)(self.s_hist.cuda_stream, self.s_plan.cuda_stream,
+                                           self.s_rr.cuda_stream)
         self.events = [torch.cuda.Event() for _ in range(2 + 2 * len(sizes))]
         cur = torch.cuda.current_stream(dev)
         for e in self.events:
@@ -452,8 +456,7 @@ class PathPipeline:
         rc = lib().ep_route_pipelined(_ptr(topk_ids), N, P, lay.ref(), self._sizes, len(self.bounds), _ptr(load),
                                       _ptr(status), _ptr(plan.phy2log), _ptr(plan.phy_quota), _ptr(plan.logcnt),
                                       _ptr(plan.log2phy), _ptr(plan.steps), _ptr(phys_ids), _ptr(self.ws),
-                                      self.ws.numel(), _stream(stream), ctypes.c_void_p(self.s_plan.cuda_stream),
-                                      ctypes.c_void_p(self.s_rr.cuda_stream), self._ev)
+                                      self.ws.numel(), _stream(stream), self._side, self._ev)
         _check(rc, "ep_route_pipelined")
 
 

@@ -4,11 +4,14 @@
 // layers planned in one launch leaves the streaming kernels idle meanwhile;
 // cut into chunks, the planner of chunk c runs while the histogram of chunk
 // c + 1 streams, and the reroute of chunk c while the planner of chunk c + 1
-// runs.  Histograms go on the caller's stream, planners on a second stream,
-// reroutes on a third; each chunk has its own histogram workspace (a slice of
-// the caller's buffer).  The outputs are those of the three calls made in
-// order on one stream.  Host-side argument checks of every launch run before
-// anything is enqueued.
+// runs.  Histograms, planners and reroutes each go on a side stream of their
+// own, and the caller's stream only orders the chain against its other work:
+// kernels overlap only across hardware queues, and three streams created one
+// after another sit on three different queues, while a side stream could share
+// the caller's (busy) one.  Each chunk has its own histogram workspace (a
+// slice of the caller's buffer).  The outputs are those of the three calls
+// made in order on one stream.  Host-side argument checks of every launch run
+// before anything is enqueued.
 #include "ep_internal.h"
 
 using namespace ep;
@@ -34,15 +37,18 @@ extern "C" int ep_route_pipelined(const int32_t *topk_ids, int64_t N, int32_t P,
                                   const int32_t *chunk_plans, int32_t num_chunks, int32_t *load,
                                   uint32_t *status, int32_t *phy2log, int32_t *phy_quota, int32_t *logcnt,
                                   int32_t *log2phy, int32_t *steps, int32_t *phys_ids, void *ws,
-                                  size_t ws_size, ep_stream_t stream, ep_stream_t plan_stream,
-                                  ep_stream_t reroute_stream, void *const *events) {
+                                  size_t ws_size, ep_stream_t stream, const ep_stream_t *side_streams,
+                                  void *const *events) {
     if (!layout || !chunk_plans || num_chunks < 1 || num_chunks > EP_MAX_CHUNKS || !events || N < 0 || P < 1)
         return EP_ERR_INVALID_ARG;
     if (!load || !status || !phy2log || !phy_quota || !logcnt || !log2phy) return EP_ERR_INVALID_ARG;
     if (N > 0 && (!topk_ids || !phys_ids)) return EP_ERR_INVALID_ARG;
-    if (!plan_stream || !reroute_stream || plan_stream == reroute_stream || plan_stream == stream ||
-        reroute_stream == stream)
-        return EP_ERR_INVALID_ARG;
+    if (!side_streams) return EP_ERR_INVALID_ARG;
+    for (int i = 0; i < 3; i++) {
+        if (!side_streams[i] || side_streams[i] == stream) return EP_ERR_INVALID_ARG;
+        for (int j = 0; j < i; j++)
+            if (side_streams[j] == side_streams[i]) return EP_ERR_INVALID_ARG;
+    }
     for (int i = 0; i < 2 + 2 * num_chunks; i++)
         if (!events[i]) return EP_ERR_INVALID_ARG;
     const int E = layout->num_experts, Phi = layout->num_phys, rho = layout->max_replicas;
@@ -79,8 +85,9 @@ extern "C" int ep_route_pipelined(const int32_t *topk_ids, int64_t N, int32_t P,
     }
 
     const hipStream_t s0 = reinterpret_cast<hipStream_t>(stream);
-    const hipStream_t sp = reinterpret_cast<hipStream_t>(plan_stream);
-    const hipStream_t sr = reinterpret_cast<hipStream_t>(reroute_stream);
+    const hipStream_t sh = reinterpret_cast<hipStream_t>(side_streams[0]);
+    const hipStream_t sp = reinterpret_cast<hipStream_t>(side_streams[1]);
+    const hipStream_t sr = reinterpret_cast<hipStream_t>(side_streams[2]);
     hipEvent_t e_start = static_cast<hipEvent_t>(events[0]);
     hipEvent_t e_done = static_cast<hipEvent_t>(events[1]);
     auto e_hist = [&](int c) { return static_cast<hipEvent_t>(events[2 + c]); };
@@ -93,6 +100,7 @@ extern "C" int ep_route_pipelined(const int32_t *topk_ids, int64_t N, int32_t P,
     } while (0)
     // the side streams start after the work already on the caller's stream
     EP_TRY(hipEventRecord(e_start, s0));
+    EP_TRY(hipStreamWaitEvent(sh, e_start, 0));
     EP_TRY(hipStreamWaitEvent(sp, e_start, 0));
     EP_TRY(hipStreamWaitEvent(sr, e_start, 0));
     int64_t a = 0;
@@ -101,8 +109,8 @@ extern "C" int ep_route_pipelined(const int32_t *topk_ids, int64_t N, int32_t P,
         const int32_t n = chunk_plans[c];
         int32_t *w = reinterpret_cast<int32_t *>(static_cast<unsigned char *>(ws) + off);
         EP_TRY(launch_histogram(N > 0 ? topk_ids + a * N : nullptr, N, n, E, sub_geom(N, n, E), w, compact_of(w, N, n, E),
-                                load + a * E, status + a, s0));
-        EP_TRY(hipEventRecord(e_hist(c), s0));
+                                load + a * E, status + a, sh));
+        EP_TRY(hipEventRecord(e_hist(c), sh));
         a += n;
         off += chunk_ws_bytes(N, n, E);
     }

@@ -206,11 +206,14 @@ def test_pipelined_route_host_checks_without_gpu():
     lay = ep._CLayout(12, 8, 16, 4, 5, 2, 1, 0, ctypes.c_void_p(16))
     fake = ctypes.c_void_p(4096)
     ev = (ctypes.c_void_p * 6)(*([4096] * 6))
-    args = lambda P, ch, n, s0, s1, s2: L.ep_route_pipelined(
-        fake, N, P, ctypes.byref(lay), ch, n, fake, fake, fake, fake, fake, fake, None, fake, fake, 1 << 20,
-        s0, s1, s2, ev)
-    s_a, s_b = ctypes.c_void_p(8), ctypes.c_void_p(24)
-    assert args(8, sizes, 2, None, s_a, s_b) == ep.EP_ERR_INVALID_ARG      # chunks sum to 7, not 8
-    assert args(7, sizes, 2, None, s_a, s_a) == ep.EP_ERR_INVALID_ARG      # one side stream twice
-    assert args(7, sizes, 2, s_a, s_a, s_b) == ep.EP_ERR_INVALID_ARG       # side stream = caller's
-    assert args(7, sizes, 0, None, s_a, s_b) == ep.EP_ERR_INVALID_ARG      # no chunk
+    def args(P, ch, n, s0, side):
+        arr = (ctypes.c_void_p * 3)(*side) if side is not None else None
+        return L.ep_route_pipelined(fake, N, P, ctypes.byref(lay), ch, n, fake, fake, fake, fake, fake, fake, None,
+                                    fake, fake, 1 << 20, s0, arr, ev)
+    s_a, s_b, s_c = 8, 24, 40
+    assert args(8, sizes, 2, None, (s_a, s_b, s_c)) == ep.EP_ERR_INVALID_ARG   # chunks sum to 7, not 8
+    assert args(7, sizes, 2, None, (s_a, s_b, s_a)) == ep.EP_ERR_INVALID_ARG   # one side stream twice
+    assert args(7, sizes, 2, s_b, (s_a, s_b, s_c)) == ep.EP_ERR_INVALID_ARG    # side stream = caller's
+    assert args(7, sizes, 2, None, (s_a, None, s_c)) == ep.EP_ERR_INVALID_ARG  # missing side stream
+    assert args(7, sizes, 2, None, None) == ep.EP_ERR_INVALID_ARG              # no side streams
+    assert args(7, sizes, 0, None, (s_a, s_b, s_c)) == ep.EP_ERR_INVALID_ARG   # no chunk
