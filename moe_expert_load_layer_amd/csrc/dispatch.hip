@@ -9,7 +9,7 @@
 //
 // One wave per sub-block (the histogram's); each workgroup builds the plan's
 // route table (slot offsets, per-instance (end, off - Q)) once and its waves
-// then walk many sub-blocks.  Every pair needs its rank among the pairs of
+// then walk one or more sub-blocks (see the launcher).  Every pair needs its rank among the pairs of
 // its expert, so each 64-pair column is ranked with an LDS bit mask per
 // expert (each lane ORs its bit, counts the bits below it) plus a per-expert
 // running count; the first rank of the expert in the sub-block comes from the
@@ -21,7 +21,8 @@
 // (its cell's offset + its rank), marks where each non-empty cell starts, and
 // then writes the staged slots in order, 64 at a time; a cell's pairs go to
 // consecutive positions, so each store writes a few coalesced runs.
-// Otherwise each pair's index is stored at its position directly.
+// Otherwise each pair's index is stored at its position directly, and the
+// launch runs plan by plan so that those scattered stores meet in the caches.
 #include <type_traits>
 
 #include "ep_internal.h"
@@ -459,13 +460,17 @@ hipError_t launch_dispatch(const int32_t *ids, int64_t N, int32_t P, const ep_la
     }
     if (w == 0) return hipErrorInvalidValue;
     const size_t lds = dispatch_lds_bytes(E, Phi, w, staged ? sub : 0, pair);
-    // Blocks per plan: every block builds the plan's route table once, so a
-    // launch of many plans uses no more blocks than the GPU holds at once
-    // (one round, equal work), each wave walking many sub-blocks.  At least one
-    // block per plan, so the slot offsets are always written.
+    // Blocks per plan.  Staged: every block builds the plan's route table once,
+    // so a launch of many plans uses no more blocks than the GPU holds at once
+    // (one round, equal work), each wave walking many sub-blocks.  Direct: one
+    // sub-block per wave; workgroups are dispatched x-fastest, so plan by plan,
+    // and the scattered 4-byte dispatch_src stores of the few plans in flight
+    // merge in the caches before they reach HBM (with every plan in flight they
+    // do not: stress batch 7.4 -> 6.4 ms).  At least one block per plan, so the
+    // slot offsets are always written.
     int64_t nblk = nsb > 0 ? (nsb + w - 1) / w : 1;
     const int resident = resident_blocks(w, staged, pair, lds);
-    if (resident > 0) {
+    if (staged && resident > 0) {
         const int64_t per_plan = resident / P > 0 ? resident / P : 1;
         if (per_plan < nblk) nblk = per_plan;
     }
