@@ -291,7 +291,8 @@ int ep_dispatch_layout(const int32_t *topk_ids, int64_t pairs_per_plan, int32_t 
  * occupies a spare slot into that slot's row of the cross-layer slot buffer
  * (UltraEP article, key designs: reserved slots, weight buffers reused across
  * layers).  One plan (one layer) per call; empty spare slots are not written.
- * Each distinct expert is read once and stored into every slot that holds it.
+ * Each distinct expert is read once (with a workspace: once per group of up to
+ * 4 of its slots) and stored into every slot that holds it.
  *   expert_weights device [E][bytes_per_expert], one layer (16-byte aligned)
  *   phy2log        device int32 [Phi], that layer's plan
  *   slot_buf       device [S][bytes_per_expert] (16-byte aligned)

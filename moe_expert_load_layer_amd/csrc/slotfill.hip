@@ -5,16 +5,16 @@
 // not written.  A pure HBM-to-HBM stream of 16-byte loads and stores.
 //
 // A hot expert often has several replicas in one plan.  Each distinct expert
-// is read once and stored into every slot that holds it, so the stream moves
-// (distinct experts + filled slots) x bytes_per_expert instead of 2 x filled
-// slots.
+// is read once per item (up to kItemSlots of its slots) and stored into every
+// slot of the item, so the stream moves about (distinct experts + filled slots)
+// x bytes_per_expert instead of 2 x filled slots.
 //
 // With a workspace (up to kListMaxSpare spare slots) the fill runs in two
 // launches:
 //   fill_list_kernel  one workgroup: the plan's fill list, i.e. the distinct
 //                     experts among the spare slots in order of their lowest
-//                     slot ("items"), and for each item the ordinals of the
-//                     slots that hold it, in ascending order;
+//                     slot, each cut into items of at most kItemSlots slots, and
+//                     for each item the ordinals of its slots, in ascending order;
 //   fill_copy_kernel  4 KiB per workgroup (one 16-byte vector per thread),
 //                     each chunk of an item read once and stored into every
 //                     slot of the item; the workgroups of one item stream
@@ -37,6 +37,14 @@ constexpr int64_t kFillChunk = (int64_t)kFillThreads * kFillUnroll;  // 16-byte 
 constexpr int kListMaxSpare = 1024;
 constexpr int kDedupMaxSpare = 1024;
 constexpr uint32_t kSuperChunks = 32;  // 4 KiB chunks an item streams before the next item
+// Slots per item: an expert held by more spare slots is read once per item of
+// at most this many slots, so no workgroup stores one chunk into more than 4
+// rows.  Long store fans kept workgroups alive for many serial stores (the
+// stress plans hold a hot expert in 20+ slots); per layer, 1 item per expert ->
+// at most 4 slots per item: stress 1131 -> 1015 us, Qwen3-like 588 -> 574 us,
+// GLM-4.5-like 465 -> 450 us, DeepSeek-V3-like unchanged (2, 3, 5, 6, 8 measured:
+// 4 is best or within 1 % everywhere).
+constexpr int kItemSlots = 4;
 
 // Weights are loaded through the caches; slot rows are stored as streaming
 // (nontemporal) writes: nothing in this launch reads them back.
@@ -46,7 +54,7 @@ constexpr uint32_t kSuperChunks = 32;  // 4 KiB chunks an item streams before th
 // ----------------------------------------------------------------- fill list
 // ws layout (int32), n = number of items:
 //   [0]                  n
-//   [1, 1 + S)           the item's expert, items in order of their lowest slot
+//   [1, 1 + S)           the item's expert, items in order of their first slot
 //   [1 + S, 2 + S + n)   the item's first target (and the total after the last)
 //   [2 + 2S, 2 + 3S)     the targets: spare ordinals grouped by item, ascending
 // A copy workgroup reads n, its item's expert and its two target bounds
@@ -66,17 +74,27 @@ __global__ __launch_bounds__(kListMaxSpare) void fill_list_kernel(const int32_t 
         key[o] = e;
     }
     __syncthreads();
-    // lowest ordinal holding the same expert, this ordinal's rank among the
-    // holders, and (for the lowest) the number of holders
+    // The slots holding one expert, in ordinal order, form items of at most
+    // kItemSlots slots.  For this ordinal: r = its rank among the expert's
+    // holders, lead = the ordinal of its item's first slot, rank = its place in
+    // the item, holders = the item's size.
     int lead = o, rank = 0, holders = 0;
     if (o < S && e >= 0) {
-        lead = -1;
+        int r = 0, all = 0;
         for (int i = 0; i < S; i++) {
             const bool same = key[i] == e;
-            if (same && lead < 0) lead = i;
-            rank += (same && i < o) ? 1 : 0;
-            holders += same ? 1 : 0;
+            r += (same && i < o) ? 1 : 0;
+            all += same ? 1 : 0;
         }
+        const int r0 = r - r % kItemSlots;
+        lead = -1;
+        for (int i = 0, c = 0; i < S; i++) {
+            const bool same = key[i] == e;
+            if (same && c == r0 && lead < 0) lead = i;
+            c += same ? 1 : 0;
+        }
+        rank = r - r0;
+        holders = all - r0 < kItemSlots ? all - r0 : kItemSlots;
     }
     const bool is_lead = o < S && e >= 0 && lead == o;
     // inclusive scan over the leaders (item count in the high half) and their

@@ -465,6 +465,8 @@ def test_deterministic_and_stream_independent(dev):
     ids = W.make_ids(wls, device=dev)
     a = ep.run_path(ids, lay)
     s2 = torch.cuda.Stream()
+    # the IDs come from work on the current stream: the side stream waits for it
+    s2.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s2):
         b = ep.run_path(ids, lay)
     s2.synchronize()
