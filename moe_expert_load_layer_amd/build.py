@@ -27,15 +27,21 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False, jobs: int = 6) -> str:
-    """Compile every csrc/*.hip for gfx950 and link libepbalance.so (always rebuilds)."""
+PHASES_LIB_PATH = os.path.join(HERE, "libepbalance_phases.so")
+
+
+def build(verbose: bool = False, jobs: int = 6, defines=(), out: str = LIB_PATH, obj_dir: str = OBJ_DIR) -> str:
+    """Compile every csrc/*.hip for gfx950 and link libepbalance.so (always rebuilds).
+
+    defines/out/obj_dir serve the planner's profiling build (plan_phases.py),
+    a separate library with the phase marks compiled in."""
     hipcc = _hipcc()
-    os.makedirs(OBJ_DIR, exist_ok=True)
+    os.makedirs(obj_dir, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
     def compile_one(src: str) -> str:
-        obj = os.path.join(OBJ_DIR, os.path.basename(src) + ".o")
-        cmd = [hipcc, *HIPCC_FLAGS, "-c", src, "-o", obj]
+        obj = os.path.join(obj_dir, os.path.basename(src) + ".o")
+        cmd = [hipcc, *HIPCC_FLAGS, *defines, "-c", src, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)
@@ -45,14 +51,20 @@ def build(verbose: bool = False, jobs: int = 6) -> str:
 
     with ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(compile_one, srcs))
-    tmp = LIB_PATH + f".tmp{os.getpid()}"
+    tmp = out + f".tmp{os.getpid()}"
     cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out)
+    return out
+
+
+def build_plan_phases(verbose: bool = False) -> str:
+    """The profiling build: libepbalance_phases.so with the planner's phase marks."""
+    return build(verbose, defines=("-DEP_PLAN_PHASES",), out=PHASES_LIB_PATH, obj_dir=os.path.join(OBJ_DIR, "phases"))
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    import sys
+    print(build_plan_phases(verbose=True) if "--plan-phases" in sys.argv[1:] else build(verbose=True))

@@ -23,6 +23,45 @@
 // A move is committed only when it lowers h's load.  Integer arithmetic only.
 #include "ep_internal.h"
 
+// Phase marks of the rank-per-lane planner for a profiling build only
+// (-DEP_PLAN_PHASES, see plan_phases.py beside the package): lane 0 accumulates
+// s_memtime stamps per phase of a move and, at the end, writes them per plan
+// to a device array that ep_plan_phases_read copies out.  In the normal build
+// the marks compile to nothing.
+#ifdef EP_PLAN_PHASES
+#define EP_PHASE_COUNT 8
+#define EP_PHASE_PLANS 256
+static __device__ unsigned long long ep_phase_buf[EP_PHASE_PLANS][16];
+#define EP_PHASE_DECL unsigned long long ph_acc_[EP_PHASE_COUNT] = {0, 0, 0, 0, 0, 0, 0, 0}, ph_t_ = 0, ph_t0_ = __builtin_amdgcn_s_memtime(), ph_tries_ = 0, ph_rank_ = 0;
+#define EP_PHASE_START() ph_t_ = __builtin_amdgcn_s_memtime();
+#define EP_PHASE(k)                                                        \
+    {                                                                      \
+        const unsigned long long t_ = __builtin_amdgcn_s_memtime();        \
+        ph_acc_[k] += t_ - ph_t_;                                          \
+        ph_t_ = t_;                                                        \
+    }
+#define EP_PHASE_COUNT_TRY() ph_tries_++;
+#define EP_PHASE_COUNT_RANK() ph_rank_++;
+#define EP_PHASE_LOOP_END() const unsigned long long ph_tl_ = __builtin_amdgcn_s_memtime();
+#define EP_PHASE_WRITE(p, lane, moves)                                                          \
+    if ((lane) == 0 && (p) < EP_PHASE_PLANS) {                                                  \
+        for (int k_ = 0; k_ < EP_PHASE_COUNT; k_++) ep_phase_buf[p][k_] = ph_acc_[k_];          \
+        ep_phase_buf[p][8] = ph_tries_;                                                         \
+        ep_phase_buf[p][9] = ph_rank_;                                                          \
+        ep_phase_buf[p][10] = (unsigned long long)(moves);                                      \
+        ep_phase_buf[p][11] = ph_tl_ - ph_t0_;                                                  \
+        ep_phase_buf[p][12] = __builtin_amdgcn_s_memtime() - ph_tl_;                            \
+    }
+#else
+#define EP_PHASE_DECL
+#define EP_PHASE_START()
+#define EP_PHASE(k)
+#define EP_PHASE_COUNT_TRY()
+#define EP_PHASE_COUNT_RANK()
+#define EP_PHASE_LOOP_END()
+#define EP_PHASE_WRITE(p, lane, moves)
+#endif
+
 namespace ep {
 namespace {
 
@@ -324,6 +363,7 @@ __global__ __launch_bounds__(kWave) void plan_kernel_lanes(const int32_t *__rest
     const int p = blockIdx.x;
     const int lane = threadIdx.x;
     const int32_t *lp = load + (int64_t)p * E;
+    EP_PHASE_DECL
 
     const bool is_rank = lane < R;
     const uint64_t rank_mask = R >= kWave ? ~0ull : ((1ull << R) - 1);
@@ -364,12 +404,14 @@ __global__ __launch_bounds__(kWave) void plan_kernel_lanes(const int32_t *__rest
     int steps = 0, cap_hit = 0;
     for (; !bad_load;) {
         if (steps == cap) { cap_hit = 1; break; }
+        EP_PHASE_START()
         // hottest rank (lowest index on ties)
         const int vmax = wave_max_i32(is_rank ? rl : -1);
         // (a ballot of one compare, masked in scalar registers, saves turning
         // a combined condition into a vector value and back)
         const int h = __ffsll((long long)(__ballot(rl == vmax) & rank_mask)) - 1;
         const int Lh = vmax;
+        EP_PHASE(0)
 
         // candidates: h's natives in lanes [0, NPR), h's spare slots in [NPR, NPR+SPR)
         int ce = -1, cq = 0, cld = 0, cic = 2, cnr = -1, cidx = 0;
@@ -399,6 +441,7 @@ __global__ __launch_bounds__(kWave) void plan_kernel_lanes(const int32_t *__rest
         const uint64_t vm = __ballot(valid);
         // candidates worth a re-level: replicated and set in edirty
         const uint64_t relevel = __ballot(valid && cic >= 2 && cdirty != 0);
+        EP_PHASE(1)
 
         bool committed = false;
         for (int pass = relevel ? 0 : 1; pass < 2 && !committed; pass++) {
@@ -431,6 +474,8 @@ __global__ __launch_bounds__(kWave) void plan_kernel_lanes(const int32_t *__rest
                     T = __builtin_amdgcn_readlane(pick(nat_ld, idx), nr);
                 }
                 const bool replicate = pass == 1;
+                EP_PHASE_COUNT_TRY()
+                EP_PHASE(2)
 
                 // instances of e on this lane's rank
                 const bool nat_here = lane == nr;
@@ -454,6 +499,7 @@ __global__ __launch_bounds__(kWave) void plan_kernel_lanes(const int32_t *__rest
                     isnew = lane == __ffsll((long long)em) - 1;
                 }
                 const bool act = inst || isnew;
+                EP_PHASE(3)
                 // sorted position by (background, rank) and inclusive prefix sum
                 int pos = 0;
                 uint32_t Sinc = (uint32_t)T;
@@ -463,7 +509,9 @@ __global__ __launch_bounds__(kWave) void plan_kernel_lanes(const int32_t *__rest
                     const bool less = bj < b || (bj == b && j < lane);
                     pos += less ? 1 : 0;
                     if (less || j == lane) Sinc += (uint32_t)bj;
+                    EP_PHASE_COUNT_RANK()
                 }
+                EP_PHASE(4)
                 // the filled instances form a prefix of the sorted order, so
                 // m* = number of instances with m*b_(m) < S_m
                 const int mstar = __popcll(__ballot(act && (uint64_t)(pos + 1) * (uint32_t)b < Sinc));
@@ -476,6 +524,7 @@ __global__ __launch_bounds__(kWave) void plan_kernel_lanes(const int32_t *__rest
                     if (act && pos < mstar) qn = (int)base - b + ((uint32_t)pos < rem ? 1 : 0);
                 }
                 const int newLh = __builtin_amdgcn_readlane(act ? b + qn : rl, h);
+                EP_PHASE(5)
                 if (newLh >= Lh) continue;
                 // commit (lane-local)
                 if (act) rl = b + qn;
@@ -511,11 +560,14 @@ __global__ __launch_bounds__(kWave) void plan_kernel_lanes(const int32_t *__rest
                 wave_lds_fence();
                 if (lane == 0) edirty[e] = 0;
                 committed = true;
+                EP_PHASE(6)
             }
         }
+        EP_PHASE(7)
         if (!committed) break;
         steps++;
     }
+    EP_PHASE_LOOP_END()
 
     // replicas left without load are freed; record each live replica's rank
 #pragma unroll
@@ -562,6 +614,7 @@ __global__ __launch_bounds__(kWave) void plan_kernel_lanes(const int32_t *__rest
         const uint32_t flags = (cap_hit ? (uint32_t)EP_STATUS_STEP_CAP : 0u) | (bad_load ? (uint32_t)EP_STATUS_BAD_LOAD : 0u);
         if (status && flags) status[p] |= flags;
     }
+    EP_PHASE_WRITE(p, lane, steps)
 }
 
 }  // namespace
@@ -620,3 +673,16 @@ hipError_t launch_plan(const int32_t *load, int32_t P, const ep_layout_t &L, int
 }
 
 }  // namespace ep
+
+#ifdef EP_PLAN_PHASES
+// Profiling build only: copies the per-plan phase cycles of the last planner
+// launch (plans [0, P), P <= 256, 16 values each: 8 phases, tries, ranking
+// iterations, moves, loop cycles, epilogue cycles) to host memory.
+extern "C" int ep_plan_phases_read(unsigned long long *host, int P) {
+    if (!host || P < 1 || P > EP_PHASE_PLANS) return EP_ERR_INVALID_ARG;
+    return hipMemcpyFromSymbol(host, HIP_SYMBOL(ep_phase_buf), (size_t)P * 16 * sizeof(unsigned long long), 0,
+                               hipMemcpyDeviceToHost) == hipSuccess
+               ? EP_OK
+               : EP_ERR_HIP;
+}
+#endif
