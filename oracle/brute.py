@@ -114,3 +114,66 @@ def slot_lower_bound(load: Sequence[int], num_ranks: int, num_spare: int) -> int
         else:
             lo = mid + 1
     return lo
+
+
+def milp_bounds(load: Sequence[int], num_ranks: int, native_rank: Sequence[int],
+                spare_count: Sequence[int], time_limit: float = 30.0):
+    """Bounds on the optimum of the same problem at sizes brute force cannot reach.
+
+    A mixed-integer program: x[e][r] in {0, 1} says that a spare slot of rank r
+    holds a copy of expert e (never on e's native rank); q[e][r] >= 0 is the
+    load expert e sends to rank r (its native rank, or a rank holding a copy:
+    q[e][r] <= load[e] * x[e][r]); the quotas of e add up to load[e]; rank r
+    holds at most spare_count[r] copies and takes at most lam in all; minimise
+    lam.  For one placement the best quotas form a transportation problem whose
+    integer optimum is the ceiling of its fractional one, so the integer optimum
+    over placements is ceil(lam*).  Solved by HiGHS (scipy.optimize.milp) within
+    ``time_limit`` seconds; returns (status, best lam found or None, proven lower
+    bound on lam*), status 0 when lam* is proven optimal.
+    """
+    from scipy.optimize import Bounds, LinearConstraint, milp
+    from scipy.sparse import csr_matrix
+
+    load = np.asarray(load, dtype=np.int64)
+    E, R = load.size, int(num_ranks)
+    spare_ranks = [r for r in range(R) if int(spare_count[r]) > 0]
+    copies = [(e, r) for e in range(E) for r in spare_ranks if int(native_rank[e]) != r and load[e] > 0]
+    nc = len(copies)
+    # variables: x[0..nc), q_native[e] at nc + e, q_copy[k] at nc + E + k, lam last
+    n = nc + E + nc + 1
+    lam = n - 1
+    rows, cols, vals, lo, hi = [], [], [], [], []
+
+    def row(entries, low, high):
+        r = len(lo)
+        for c, v in entries:
+            rows.append(r); cols.append(c); vals.append(v)
+        lo.append(low); hi.append(high)
+
+    by_expert = [[] for _ in range(E)]
+    by_rank = {r: [] for r in spare_ranks}
+    for k, (e, r) in enumerate(copies):
+        by_expert[e].append(k)
+        by_rank[r].append(k)
+    for e in range(E):
+        row([(nc + e, 1.0)] + [(nc + E + k, 1.0) for k in by_expert[e]], float(load[e]), float(load[e]))
+    for k, (e, r) in enumerate(copies):
+        row([(nc + E + k, 1.0), (k, -float(load[e]))], -np.inf, 0.0)
+    for r in spare_ranks:
+        row([(k, 1.0) for k in by_rank[r]], -np.inf, float(spare_count[r]))
+    for r in range(R):
+        entries = [(nc + e, 1.0) for e in range(E) if int(native_rank[e]) == r]
+        entries += [(nc + E + k, 1.0) for k in by_rank.get(r, [])]
+        row(entries + [(lam, -1.0)], -np.inf, 0.0)
+    A = csr_matrix((vals, (rows, cols)), shape=(len(lo), n))
+    c = np.zeros(n)
+    c[lam] = 1.0
+    integrality = np.zeros(n)
+    integrality[:nc] = 1
+    upper = np.concatenate([np.ones(nc), np.full(E + nc + 1, np.inf)])
+    res = milp(c, constraints=LinearConstraint(A, lo, hi), integrality=integrality,
+               bounds=Bounds(np.zeros(n), upper), options={"time_limit": float(time_limit)})
+    best = float(res.fun) if res.fun is not None else None
+    bound = getattr(res, "mip_dual_bound", None)
+    bound = float(bound) if bound is not None else (best if res.status == 0 else 0.0)
+    return int(res.status), best, bound
