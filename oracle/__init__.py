@@ -6,8 +6,8 @@ Python binding) never imports it, and the two share no code.
 
 The arithmetic lives in ``ep_oracle.c`` (plain single-threaded C, built with gcc
 by :func:`oracle.build.build`); this module only marshals numpy arrays.  The
-exact optimum for tiny instances and the slot-count lower bound are in
-:mod:`oracle.brute`.
+exact optimum for tiny instances, the slot-count lower bound and the MILP bounds
+for full-size plans are in :mod:`oracle.brute`.
 """
 from __future__ import annotations
 
