@@ -27,7 +27,9 @@ pair with the count rows), and the slot fill reads each distinct expert once for
 all the slots that hold it ((distinct experts + filled slots) x bytes_per_expert).
 
 The roofline object covers the dominant kernel, the slot fill: `achieved` and
-`frac` on the first rule, `achieved_moved` and `frac_moved` on the bytes moved,
+`frac` on the first rule (which can pass 1.0: the fill reads a replicated expert
+once for up to four of its slots, so it moves fewer bytes than that rule counts),
+`achieved_moved` and `frac_moved` on the bytes moved,
 from the mean launch time measured with HIP events on the stream the fills run
 on.  `traffic` is the HBM bytes per launch from the rocprofv3 FETCH_SIZE and
 WRITE_SIZE summary committed for this kernel source (null when the source has
