@@ -320,8 +320,8 @@ __global__ __launch_bounds__(kWave) void plan_kernel_generic(const int32_t *__re
 //
 // Lane r owns rank r.  In registers: its load, free spare count, its native
 // experts (ID, load, quota, instance count) and its spare slots (owner,
-// quota).  Candidates on the hottest rank come from that lane's registers by
-// readlane; the instances of an expert are found lane-locally (its native
+// quota, and the owner's native rank, index and load).  Candidates on the
+// hottest rank come from that lane's registers by readlane; the instances of an expert are found lane-locally (its native
 // lane, or a lane holding it in a spare slot); the water-fill runs over the
 // lanes that host the expert and a commit only touches their registers.  LDS
 // holds the static (native rank, native index) of every expert, a per-expert
@@ -354,7 +354,7 @@ __global__ __launch_bounds__(kWave) void plan_kernel_lanes(const int32_t *__rest
     extern __shared__ __align__(16) unsigned char sh_raw[];
     uint64_t *emask = reinterpret_cast<uint64_t *>(sh_raw);      // [E] ranks of live replicas
     int32_t *nri = reinterpret_cast<int32_t *>(emask + E);       // [E] native rank << 8 | index
-    // [E] set when a move of another expert changed the load of a rank that
+    // [E + 1] set when a move of another expert changed the load of a rank that
     // hosts this expert after the expert was last water-filled; re-levelling
     // an expert that is not set would reproduce its current quotas, so such
     // candidates are skipped
@@ -372,7 +372,9 @@ __global__ __launch_bounds__(kWave) void plan_kernel_lanes(const int32_t *__rest
     const int spc = is_rank ? a.T.rank_first[lane + 1] - f0 - nat : 0;
     int freec = spc;
     int32_t nat_e[NPR], nat_ld[NPR], nat_q[NPR], nat_ic[NPR];
-    int32_t sp_owner[SPR], sp_q[SPR];
+    // a spare slot's owner and quota, and the owner's native rank << 8 | index
+    // and load (copied when the replica is made)
+    int32_t sp_owner[SPR], sp_q[SPR], sp_nri[SPR], sp_ld[SPR];
 #pragma unroll
     for (int i = 0; i < NPR; i++) nat_e[i] = i < nat ? a.T.slot_home[f0 + i] : -1;
 #pragma unroll
@@ -383,8 +385,9 @@ __global__ __launch_bounds__(kWave) void plan_kernel_lanes(const int32_t *__rest
         if (nat_e[i] >= 0) nri[nat_e[i]] = (lane << 8) | i;
     }
 #pragma unroll
-    for (int j = 0; j < SPR; j++) { sp_owner[j] = -1; sp_q[j] = 0; }
-    for (int e = lane; e < E; e += kWave) { emask[e] = 0; edirty[e] = 0; }
+    for (int j = 0; j < SPR; j++) { sp_owner[j] = -1; sp_q[j] = 0; sp_nri[j] = 0; sp_ld[j] = 0; }
+    for (int e = lane; e <= E; e += kWave) edirty[e] = 0;  // entry E stays clear: empty slots read it
+    for (int e = lane; e < E; e += kWave) emask[e] = 0;
     int rl = 0;
     int64_t lsum = 0;
     bool lneg = false;
@@ -405,6 +408,27 @@ __global__ __launch_bounds__(kWave) void plan_kernel_lanes(const int32_t *__rest
     for (; !bad_load;) {
         if (steps == cap) { cap_hit = 1; break; }
         EP_PHASE_START()
+        // The hottest rank's loaded instance slots are the candidates (slot
+        // k < NPR its k-th native, NPR + j its j-th spare).  A pass tries them
+        // in descending (quota, -expert) order, each found when needed (most
+        // steps commit on the first one): the largest quota left, the lowest
+        // expert among equal quotas (the experts of one rank are distinct).
+        // With few slots per rank the slots are read into scalar registers and
+        // compared there (no wave reduction: Qwen3-like plans 3.5 % faster);
+        // with more, one slot per lane and a wave reduction per pick (a
+        // scalar pick over 8 slots was 2 % slower).
+        constexpr int K = NPR + SPR;
+        constexpr bool kScalarPick = K <= 5;
+        uint32_t db = 0;
+        if constexpr (kScalarPick) {
+            // re-level flags of this lane's slots (LDS reads issued ahead of
+            // the reduction, which hides their latency)
+#pragma unroll
+            for (int i = 0; i < NPR; i++) db |= (edirty[nat_e[i] >= 0 ? nat_e[i] : E] != 0 ? 1u : 0u) << i;
+#pragma unroll
+            for (int j = 0; j < SPR; j++)
+                db |= (edirty[sp_owner[j] >= 0 ? sp_owner[j] : E] != 0 ? 1u : 0u) << (NPR + j);
+        }
         // hottest rank (lowest index on ties)
         const int vmax = wave_max_i32(is_rank ? rl : -1);
         // (a ballot of one compare, masked in scalar registers, saves turning
@@ -413,65 +437,103 @@ __global__ __launch_bounds__(kWave) void plan_kernel_lanes(const int32_t *__rest
         const int Lh = vmax;
         EP_PHASE(0)
 
-        // candidates: h's natives in lanes [0, NPR), h's spare slots in [NPR, NPR+SPR)
-        int ce = -1, cq = 0, cld = 0, cic = 2, cnr = -1, cidx = 0;
+        uint64_t vm, relevel;        // loaded slots; those worth a re-level (replicated, flag set)
+        uint32_t sq[kScalarPick ? K : 1];
+        int32_t se[kScalarPick ? K : 1];
+        int ce = -1, cq = 0, cld = 0, cpk = 0;  // lane k: slot k's expert, quota, load, native
+        if constexpr (kScalarPick) {
+            uint32_t vb = 0, rb = 0;
 #pragma unroll
-        for (int i = 0; i < NPR; i++) {
-            const int e = __builtin_amdgcn_readlane(nat_e[i], h);
-            const int q = __builtin_amdgcn_readlane(nat_q[i], h);
-            const int l = __builtin_amdgcn_readlane(nat_ld[i], h);
-            const int ic = __builtin_amdgcn_readlane(nat_ic[i], h);
-            if (lane == i) { ce = e; cq = q; cld = l; cic = ic; cnr = h; cidx = i; }
-        }
+            for (int i = 0; i < NPR; i++) {
+                vb |= (nat_q[i] > 0 ? 1u : 0u) << i;
+                rb |= (nat_ic[i] >= 2 ? 1u : 0u) << i;
+            }
 #pragma unroll
-        for (int j = 0; j < SPR; j++) {
-            const int e = __builtin_amdgcn_readlane(sp_owner[j], h);
-            const int q = __builtin_amdgcn_readlane(sp_q[j], h);
-            if (lane == NPR + j) { ce = e; cq = q; }
+            for (int j = 0; j < SPR; j++) {
+                vb |= (sp_q[j] > 0 ? 1u : 0u) << (NPR + j);
+                rb |= 1u << (NPR + j);
+            }
+            rb &= vb & db;
+            vm = (uint32_t)__builtin_amdgcn_readlane((int)vb, h);
+            relevel = (uint32_t)__builtin_amdgcn_readlane((int)rb, h);
+#pragma unroll
+            for (int i = 0; i < NPR; i++) {
+                sq[i] = (uint32_t)__builtin_amdgcn_readlane(nat_q[i], h);
+                se[i] = __builtin_amdgcn_readlane(nat_e[i], h);
+            }
+#pragma unroll
+            for (int j = 0; j < SPR; j++) {
+                sq[NPR + j] = (uint32_t)__builtin_amdgcn_readlane(sp_q[j], h);
+                se[NPR + j] = __builtin_amdgcn_readlane(sp_owner[j], h);
+            }
+        } else {
+            int cic = 2;
+#pragma unroll
+            for (int i = 0; i < NPR; i++) {
+                const int e = __builtin_amdgcn_readlane(nat_e[i], h);
+                const int q = __builtin_amdgcn_readlane(nat_q[i], h);
+                const int l = __builtin_amdgcn_readlane(nat_ld[i], h);
+                const int ic = __builtin_amdgcn_readlane(nat_ic[i], h);
+                if (lane == i) { ce = e; cq = q; cld = l; cic = ic; cpk = (h << 8) | i; }
+            }
+#pragma unroll
+            for (int j = 0; j < SPR; j++) {
+                const int e = __builtin_amdgcn_readlane(sp_owner[j], h);
+                const int q = __builtin_amdgcn_readlane(sp_q[j], h);
+                const int pk = __builtin_amdgcn_readlane(sp_nri[j], h);
+                const int l = __builtin_amdgcn_readlane(sp_ld[j], h);
+                if (lane == NPR + j) { ce = e; cq = q; cpk = pk; cld = l; }
+            }
+            const bool valid = ce >= 0 && cq > 0;
+            const int cdirty = valid ? edirty[ce] : 0;
+            vm = __ballot(valid);
+            relevel = __ballot(valid && cic >= 2 && cdirty != 0);
         }
-        const bool valid = ce >= 0 && cq > 0;
-        // LDS reads of the candidates: dirty flag; native rank and index of a
-        // replica's expert (skipping them when no candidate is replicated
-        // measured slower: the extra ballot costs more than the read)
-        int cdirty = 0, cpk = 0;
-        if (valid) {
-            cdirty = edirty[ce];
-            if (cnr < 0) cpk = nri[ce];
-        }
-        const uint64_t vm = __ballot(valid);
-        // candidates worth a re-level: replicated and set in edirty
-        const uint64_t relevel = __ballot(valid && cic >= 2 && cdirty != 0);
         EP_PHASE(1)
 
         bool committed = false;
         for (int pass = relevel ? 0 : 1; pass < 2 && !committed; pass++) {
-            // the pass's candidates in descending (quota, -expert) order, each
-            // found when needed (most steps commit on the first one): the
-            // largest quota left, the lowest expert among equal quotas (the
-            // experts on one rank are distinct)
             uint64_t left = pass == 0 ? relevel : vm;
             while (left && !committed) {
-                const bool in = (left >> lane) & 1;
-                const int qmax = wave_max_i32(in ? cq : -1);
-                uint64_t tm = __ballot(cq == qmax) & left;
-                if (tm & (tm - 1)) {
-                    const bool tie = (tm >> lane) & 1;
-                    const int emin = wave_min_i32(tie ? ce : 0x7fffffff);
-                    tm &= __ballot(ce == emin);
-                }
-                const int cl = __ffsll((long long)tm) - 1;
-                left &= ~(1ull << cl);
-                const int e = __builtin_amdgcn_readlane(ce, cl);
-                int nr = __builtin_amdgcn_readlane(cnr, cl);
-                int idx, T;
-                if (nr >= 0) {
-                    idx = __builtin_amdgcn_readlane(cidx, cl);
-                    T = __builtin_amdgcn_readlane(cld, cl);
+                int e, nr, idx, T;
+                if constexpr (kScalarPick) {
+                    int bk = 0;
+                    uint32_t bq = 0;
+                    e = 0x7fffffff;
+#pragma unroll
+                    for (int k = 0; k < K; k++) {
+                        const bool better = ((left >> k) & 1u) && (sq[k] > bq || (sq[k] == bq && se[k] < e));
+                        bk = better ? k : bk;
+                        bq = better ? sq[k] : bq;
+                        e = better ? se[k] : e;
+                    }
+                    left &= ~(1ull << bk);
+                    if (bk < NPR) {
+                        nr = h;
+                        idx = bk;
+                        T = __builtin_amdgcn_readlane(pick(nat_ld, bk), h);
+                    } else {
+                        const int pk = __builtin_amdgcn_readlane(pick(sp_nri, bk - NPR), h);
+                        nr = pk >> 8;
+                        idx = pk & 0xff;
+                        T = __builtin_amdgcn_readlane(pick(sp_ld, bk - NPR), h);
+                    }
                 } else {
-                    const int packed = __builtin_amdgcn_readlane(cpk, cl);
-                    nr = packed >> 8;
-                    idx = packed & 0xff;
-                    T = __builtin_amdgcn_readlane(pick(nat_ld, idx), nr);
+                    const bool in = (left >> lane) & 1;
+                    const int qmax = wave_max_i32(in ? cq : -1);
+                    uint64_t tm = __ballot(cq == qmax) & left;
+                    if (tm & (tm - 1)) {
+                        const bool tie = (tm >> lane) & 1;
+                        const int emin = wave_min_i32(tie ? ce : 0x7fffffff);
+                        tm &= __ballot(ce == emin);
+                    }
+                    const int cl = __ffsll((long long)tm) - 1;
+                    left &= ~(1ull << cl);
+                    e = __builtin_amdgcn_readlane(ce, cl);
+                    const int pk = __builtin_amdgcn_readlane(cpk, cl);
+                    nr = pk >> 8;
+                    idx = pk & 0xff;
+                    T = __builtin_amdgcn_readlane(cld, cl);
                 }
                 const bool replicate = pass == 1;
                 EP_PHASE_COUNT_TRY()
@@ -544,7 +606,7 @@ __global__ __launch_bounds__(kWave) void plan_kernel_lanes(const int32_t *__rest
                     const int jn = spc - freec;
 #pragma unroll
                     for (int j = 0; j < SPR; j++)
-                        if (j == jn) { sp_owner[j] = e; sp_q[j] = qn; }
+                        if (j == jn) { sp_owner[j] = e; sp_q[j] = qn; sp_nri[j] = (nr << 8) | idx; sp_ld[j] = T; }
                     freec -= 1;
                 }
                 // every expert on a rank whose load moved needs a new level,
@@ -624,7 +686,7 @@ size_t plan_lds_bytes(const ep_layout_t &L) {
     return 8 * E + 8 * kWave + 4 * (5 * R + 1 + 3 * Phi + 5 * E + S + kWave);
 }
 
-static size_t lanes_lds_bytes(const ep_layout_t &L) { return (size_t)L.num_experts * 16; }
+static size_t lanes_lds_bytes(const ep_layout_t &L) { return (size_t)L.num_experts * 16 + 16; }
 
 static int pow2_at_least(int x) {
     int v = 1;
