@@ -554,7 +554,7 @@ def main(argv=None) -> int:
                                                 dispatch_src=dsrc), 5) * 1e-3
     next_rows = {"dispatch_layout_ms": disp_ms,
                  "dispatch_layout_GBps": 12.0 * P * N / (disp_ms * 1e-3) / 1e9}
-    # backward: fold replica gradients (fp32, 3x4096x1536 per expert) into the
+    # backward: fold replica gradients (fp32, one expert's element count) into the
     # native rows for layer 0's plan
     n_el = bpe // 2
     g_native = torch.zeros((E, n_el), dtype=torch.float32, device=dev)
@@ -597,9 +597,11 @@ def main(argv=None) -> int:
         "data": "synthetic (seeded Dirichlet(0.3) top-8 routing, bf16 N(0,1) expert weights)",
         "config": {"workload": f"{wl.name}: E={E} top-{wl.top_k} EP{wl.num_ranks} "
                                f"{wl.tokens_per_rank} tokens/rank, {P} layers, {S} spare slots, "
-                               f"expert 3x4096x1536 bf16",
+                               f"expert {'x'.join(map(str, wl.expert_shape))} bf16",
                    "pairs_per_step": P * N, "plans_per_step": P},
-        "roofline": {"bound": "hbm", "kernel": "fill_copy_kernel",
+        # the events bracket one ep_slot_fill call: the one-workgroup list
+        # kernel (about 1 % of it) and the copy kernel
+        "roofline": {"bound": "hbm", "kernel": "ep_slot_fill (fill_list_kernel + fill_copy_kernel)",
                      "achieved": fill["GBps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": fill["frac"], "traffic": traffic,
                      "bytes_rule": FILL_RULE, "bytes_per_launch": fill["bytes"],
