@@ -18,7 +18,7 @@
 //
 // dispatch_src is written through LDS when the staging buffer leaves enough
 // waves resident: each wave stages the in-sub-block index of every pair at
-// (its cell's offset + its rank), marks where each non-empty cell starts, and
+// (its cell's offset + its rank), marks where each non-empty cell ends, and
 // then writes the staged slots in order, 64 at a time; a cell's pairs go to
 // consecutive positions, so each store writes a few coalesced runs.
 // Otherwise each pair's index is stored at its position directly, and the
@@ -30,12 +30,17 @@
 namespace ep {
 namespace {
 
-// Per-expert state of a wave's sub-block (16 bytes): the bit mask of the
+// Per-expert state of a wave's sub-block (a "cell"): the bit mask of the
 // current 64-pair column, the count of the expert's pairs in earlier columns
 // with two flags in its top bits, and the position base: run + (off - Q) of
 // the one instance that takes all of the expert's pairs here, or the run
 // itself when a quota boundary falls inside (split), so that the k-th pair
 // of the cell goes to base + k, or to the instance a search of run + k finds.
+// In LDS the fields live in separate arrays over the experts (masks, then
+// (count, base) pairs): the column's 8-byte mask accesses of neighbouring
+// experts then fall in neighbouring banks (with 16-byte cells the bank
+// conflicts were 45 % higher and the Qwen3-like batch 2-8 % slower).  These
+// structs hold one cell's values in registers.
 struct Cell1 {
     uint64_t mask;
     uint32_t kf;
@@ -48,15 +53,6 @@ struct Cell2 {
     uint32_t kf;
     int32_t base;
 };
-template <bool PAIR> using CellOf = typename std::conditional<PAIR, Cell2, Cell1>::type;
-template <bool PAIR> __device__ __forceinline__ CellOf<PAIR> make_cell(uint32_t kf, int32_t base) {
-    CellOf<PAIR> c;
-    c.mask = 0ull;
-    if constexpr (PAIR) c.mask1 = 0ull;
-    c.kf = kf;
-    c.base = base;
-    return c;
-}
 constexpr uint32_t kSplitFlag = 1u << 30;  // a quota boundary falls inside the cell
 constexpr uint32_t kNoneFlag = 1u << 31;   // no instance takes these pairs
 constexpr uint32_t kCountMask = kSplitFlag - 1;
@@ -81,17 +77,21 @@ __global__ __launch_bounds__(W *kWave) void dispatch_kernel(
     const int64_t nwords = STAGED ? sub / kWave : 0;                         // cell-start bit words
     const int E1c = E + 1;                                                  // cell E: padding, bad IDs
     const int64_t sstride = STAGED ? sub + kWave : 0;                       // slot sub: sink
-    using Cell = CellOf<PAIR>;
-    Cell *cell_all = reinterpret_cast<Cell *>(sh_raw);                      // [W][E+1]
-    uint64_t *sbits_all = reinterpret_cast<uint64_t *>(cell_all + (size_t)W * E1c); // [W][sub/64] if STAGED
+    // a wave's cells: column masks [E+1] (two arrays if PAIR), then (count
+    // with flags, base) [E+1]
+    constexpr int kCellWords = PAIR ? 3 : 2;
+    uint64_t *cell_all = reinterpret_cast<uint64_t *>(sh_raw);              // [W][kCellWords][E+1]
+    uint64_t *sbits_all = cell_all + (size_t)W * kCellWords * E1c;           // [W][sub/64] if STAGED
     int2 *inst = reinterpret_cast<int2 *>(sbits_all + (size_t)W * nwords);  // [Phi] (end, off - Q)
     int32_t *soff = reinterpret_cast<int32_t *>(inst + Phi);                // [Phi + 1]
     int32_t *rfirst = soff + Phi + 1;                                       // [E]
     int32_t *rcnt = rfirst + E;                                             // [E]
-    int32_t *nel_all = rcnt + E;                                            // [W][E] if STAGED
-    int32_t *off_all = nel_all + (STAGED ? (size_t)W * E : 0);              // [W][E] if STAGED
+    int32_t *nel_all = rcnt + E;                                            // [W][E+1] if STAGED
+    int32_t *off_all = nel_all + (STAGED ? (size_t)W * (E + 1) : 0);        // [W][E] if STAGED
     uint16_t *stage_all = reinterpret_cast<uint16_t *>(off_all + (STAGED ? (size_t)W * E : 0)); // [W][sub + 64]
-    const int wave = threadIdx.x / kWave;
+    // (the wave index is uniform in a wave: read into a scalar register, so
+    // that the sub-block loop, its bounds and bases stay scalar)
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int lane = threadIdx.x % kWave;
     const int p = blockIdx.y;
     const int E1 = E + 1;
@@ -169,11 +169,13 @@ __global__ __launch_bounds__(W *kWave) void dispatch_kernel(
     // reusing the block's route table; no block barriers below
     for (int64_t sb = (int64_t)blockIdx.x * W + wave; sb < nsb; sb += (int64_t)gridDim.x * W) {
     wave_lds_fence();  // the previous sub-block's reads of the wave's LDS are done
-    Cell *cells = cell_all + (size_t)wave * E1c;
+    uint64_t *mk0 = cell_all + (size_t)wave * kCellWords * E1c;
+    uint64_t *mk1 = mk0 + E1c;  // PAIR only
+    uint2 *inf = reinterpret_cast<uint2 *>(mk0 + (size_t)(kCellWords - 1) * E1c);
     int32_t *offs = off_all + (size_t)wave * (STAGED ? E : 0);  // staging offset of each cell
     uint16_t *stage = stage_all + (size_t)wave * sstride;
-    uint64_t *sbits = sbits_all + (size_t)wave * nwords;   // bit t: staged slot t starts a cell
-    int32_t *nel = nel_all + (size_t)wave * (STAGED ? E : 0);  // non-empty cells' experts, in order
+    uint64_t *sbits = sbits_all + (size_t)wave * nwords;   // bit t: staged slot t ends a cell
+    int32_t *nel = nel_all + (size_t)wave * (STAGED ? E + 1 : 0);  // non-empty cells' experts, in order
     const SubPrefix pre = sub_prefix(ws, p, sb, nsb, sps, nseg, E1);
     int staged_pairs = 0;
     if (STAGED) {
@@ -210,7 +212,9 @@ __global__ __launch_bounds__(W *kWave) void dispatch_kernel(
             const int incl = wave_incl_scan_i32(cnt);
             const int off = carry + incl - cnt;
             if (e < E) {
-                cells[e] = make_cell<PAIR>(flags, base);
+                mk0[e] = 0ull;
+                if (PAIR) mk1[e] = 0ull;
+                inf[e] = make_uint2(flags, (uint32_t)base);
                 if (STAGED) offs[e] = off;
             }
             if (STAGED) {
@@ -218,15 +222,22 @@ __global__ __launch_bounds__(W *kWave) void dispatch_kernel(
                 const uint64_t fm = __ballot(full);
                 if (full) {
                     nel[ncells + __popcll(fm & lanemask_lt())] = e;
-                    atomicOr(reinterpret_cast<unsigned long long *>(&sbits[off / kWave]),
-                             1ull << (off % kWave));
+                    const int last = off + cnt - 1;
+                    atomicOr(reinterpret_cast<unsigned long long *>(&sbits[last / kWave]),
+                             1ull << (last % kWave));
                 }
                 ncells += __popcll(fm);
             }
             carry += __shfl(incl, kWave - 1);
         }
-        staged_pairs = carry;
-        if (lane == 0) cells[E] = make_cell<PAIR>(kNoneFlag, 0);
+        // (uniform: the flush loop below then runs on scalar registers)
+        staged_pairs = __builtin_amdgcn_readfirstlane(carry);
+        if (STAGED && lane == 0) nel[ncells] = 0;  // read by slots past the staged pairs
+        if (lane == 0) {
+            mk0[E] = 0ull;
+            if (PAIR) mk1[E] = 0ull;
+            inf[E] = make_uint2(kNoneFlag, 0u);
+        }
     }
     wave_lds_fence();
 
@@ -238,18 +249,28 @@ __global__ __launch_bounds__(W *kWave) void dispatch_kernel(
     const uint64_t lt = lanemask_lt();
     const uint64_t bit = 1ull << lane;
     const uint32_t uE = (uint32_t)E;
+    // pair offsets within the sub-block are 32-bit (a sub-block is far below
+    // 2^30 pairs), so the loads and the position stores address from a
+    // scalar base plus a 32-bit byte offset (with 64-bit indices the kernel
+    // issued 6 % more vector instructions and held 120 instead of 71
+    // registers)
+    const char *srcb = reinterpret_cast<const char *>(src + begin);
+    char *posb = reinterpret_cast<char *>(pos_out + begin);
+    const uint32_t len = (uint32_t)(end - begin);
+    const uint32_t lastu = len - 1;
+    const int32_t Ni = (int32_t)N;  // N < 2^31 (the API's bound)
+    auto ld_id = [&](uint32_t o) -> int32_t {
+        const uint32_t oc = o < lastu ? o : lastu;
+        const int32_t t = __builtin_nontemporal_load(reinterpret_cast<const int32_t *>(srcb + (oc << 2)));
+        return o < len ? t : -1;
+    };
     constexpr int U = 8;
     // the IDs of the next U columns load while the current ones are ranked
     // (the loads are unconditional, from a clamped index, so that the wait
     // for a group's IDs does not also wait for the next group's)
-    const int64_t last = end - 1;
     int32_t nxt[U];
 #pragma unroll
-    for (int u = 0; u < U; u++) {
-        const int64_t i = begin + u * kWave + lane;
-        const int32_t t = __builtin_nontemporal_load(src + (i < end ? i : last));
-        nxt[u] = i < end ? t : -1;
-    }
+    for (int u = 0; u < U; u++) nxt[u] = ld_id((uint32_t)(u * kWave + lane));
     // whole groups of U columns store every pair's position unconditionally:
     // a store under a branch leaves the compiler unable to count the stores
     // issued after the prefetched ID loads, and its wait for those loads then
@@ -257,13 +278,19 @@ __global__ __launch_bounds__(W *kWave) void dispatch_kernel(
     auto group = [&](int64_t g, auto fullc) {
         constexpr bool FULL = decltype(fullc)::value;
         int32_t v[U];
+        const uint32_t go = (uint32_t)(g - begin);
 #pragma unroll
-        for (int u = 0; u < U; u++) {
-            v[u] = nxt[u];
-            const int64_t i = g + (U + u) * kWave + lane;
-            const int32_t t = __builtin_nontemporal_load(src + (i < end ? i : last));
-            nxt[u] = i < end ? t : -1;
+        for (int u = 0; u < U; u++) v[u] = nxt[u];
+        if (go + 2 * U * kWave <= len) {
+            // the next group is whole: one address, the columns at immediate offsets
+            const int32_t *q = reinterpret_cast<const int32_t *>(srcb + ((go + U * kWave + (uint32_t)lane) << 2));
+#pragma unroll
+            for (int u = 0; u < U; u++) nxt[u] = __builtin_nontemporal_load(q + u * kWave);
+        } else {
+#pragma unroll
+            for (int u = 0; u < U; u++) nxt[u] = ld_id(go + (uint32_t)((U + u) * kWave + lane));
         }
+        int32_t *pq = reinterpret_cast<int32_t *>(posb + ((go + (uint32_t)lane) << 2));
         if constexpr (PAIR) {
             // two columns per LDS round trip: each ORs its lanes into its own
             // mask of the expert's cell, one read then ranks both (a pair in the
@@ -276,33 +303,53 @@ __global__ __launch_bounds__(W *kWave) void dispatch_kernel(
                 const int32_t xa = v[u], xb = v[u + 1];
                 const bool va = (uint32_t)xa < uE, vb = (uint32_t)xb < uE;
                 const int ia = va ? xa : E, ib = vb ? xb : E;  // padding and bad IDs rank in the sink cell
-                atomicOr(reinterpret_cast<unsigned long long *>(&cells[ia].mask), bit);
-                atomicOr(reinterpret_cast<unsigned long long *>(&cells[ib].mask1), bit);
+                atomicOr(reinterpret_cast<unsigned long long *>(&mk0[ia]), bit);
+                atomicOr(reinterpret_cast<unsigned long long *>(&mk1[ib]), bit);
                 wave_lds_fence();
-                const Cell ca = cells[ia];
-                const Cell cb = cells[ib];
-                const int32_t offa = STAGED && va ? offs[ia] : 0;
-                const int32_t offb = STAGED && vb ? offs[ib] : 0;
+                Cell2 ca, cb;
+                ca.mask = mk0[ia];
+                ca.mask1 = mk1[ia];
+                {
+                    const uint2 t = inf[ia];
+                    ca.kf = t.x;
+                    ca.base = (int32_t)t.y;
+                }
+                cb.mask = mk0[ib];
+                cb.mask1 = mk1[ib];
+                {
+                    const uint2 t = inf[ib];
+                    cb.kf = t.x;
+                    cb.base = (int32_t)t.y;
+                }
+                const int32_t offa = STAGED ? offs[va ? ia : 0] : 0;
+                const int32_t offb = STAGED ? offs[vb ? ib : 0] : 0;
                 wave_lds_fence();
                 const uint64_t belowa = ca.mask & lt;
                 const uint64_t belowb = cb.mask1 & lt;
                 // one lane per expert of the pair: its lowest in the first column,
                 // else (absent there) its lowest in the second
-                if (belowa == 0)
-                    cells[ia] = make_cell<PAIR>(ca.kf + (uint32_t)__popcll(ca.mask) + (uint32_t)__popcll(ca.mask1), ca.base);
-                if (cb.mask == 0 && belowb == 0)
-                    cells[ib] = make_cell<PAIR>(cb.kf + (uint32_t)__popcll(cb.mask1), cb.base);
+                if (belowa == 0) {
+                    mk0[ia] = 0ull;
+                    mk1[ia] = 0ull;
+                    inf[ia].x = ca.kf + (uint32_t)__popcll(ca.mask) + (uint32_t)__popcll(ca.mask1);
+                }
+                if (cb.mask == 0 && belowb == 0) {
+                    mk1[ib] = 0ull;
+                    inf[ib].x = cb.kf + (uint32_t)__popcll(cb.mask1);
+                }
                 const int32_t ka = (int32_t)(ca.kf & kCountMask) + (int32_t)__popcll(belowa);
                 const int32_t kb = (int32_t)(cb.kf & kCountMask) + (int32_t)__popcll(cb.mask) + (int32_t)__popcll(belowb);
-                auto place = [&](const Cell &c, int xi, bool valid, int32_t off, int32_t k, int64_t i) {
+                auto place = [&](const Cell2 &c, int xi, bool valid, int32_t off, int32_t k, int col) {
+                    const uint32_t o = go + (uint32_t)(col * kWave + lane);
                     int32_t pos = (c.kf & (kNoneFlag | kSplitFlag)) ? -1 : c.base + k;
                     if (c.kf & kSplitFlag) pos = position_of(inst, rfirst[xi], rcnt[xi], c.base + k);
-                    if (STAGED) stage[valid ? off + k : sub] = (uint16_t)(i - begin);
-                    else if (pos >= 0 && pos < N) src_out[pos] = (int32_t)i;
-                    if (FULL || i < end) __builtin_nontemporal_store(pos, pos_out + i);
+                    if (STAGED) stage[valid ? off + k : sub] = (uint16_t)o;
+                    else if ((uint32_t)pos < (uint32_t)Ni) src_out[pos] = (int32_t)(begin + o);
+                    if (FULL) __builtin_nontemporal_store(pos, pq + col * kWave);
+                    else if (o < len) __builtin_nontemporal_store(pos, reinterpret_cast<int32_t *>(posb + (o << 2)));
                 };
-                place(ca, ia, va, offa, ka, g + u * kWave + lane);
-                place(cb, ib, vb, offb, kb, g + (u + 1) * kWave + lane);
+                place(ca, ia, va, offa, ka, u);
+                place(cb, ib, vb, offb, kb, u + 1);
                 wave_lds_fence();
             }
     
@@ -312,20 +359,32 @@ __global__ __launch_bounds__(W *kWave) void dispatch_kernel(
                 const int32_t x = v[u];
                 const bool valid = (uint32_t)x < uE;
                 const int xi = valid ? x : E;  // padding and bad IDs rank in the sink cell
-                atomicOr(reinterpret_cast<unsigned long long *>(&cells[xi].mask), bit);
+                atomicOr(reinterpret_cast<unsigned long long *>(&mk0[xi]), bit);
                 wave_lds_fence();
-                const Cell cur = cells[xi];
-                const int32_t off = STAGED && valid ? offs[xi] : 0;
+                Cell1 cur;
+                cur.mask = mk0[xi];
+                {
+                    const uint2 t = inf[xi];
+                    cur.kf = t.x;
+                    cur.base = (int32_t)t.y;
+                }
+                // (read by every lane, the sink's lanes from cell 0: a read
+                // under a branch gets a wait of its own)
+                const int32_t off = STAGED ? offs[valid ? xi : 0] : 0;
                 wave_lds_fence();
-                const int64_t i = g + u * kWave + lane;
+                const uint32_t o = go + (uint32_t)(u * kWave + lane);
                 const uint64_t below = cur.mask & lt;
-                if (below == 0) cells[xi] = make_cell<PAIR>(cur.kf + (uint32_t)__popcll(cur.mask), cur.base);
+                if (below == 0) {
+                    mk0[xi] = 0ull;
+                    inf[xi].x = cur.kf + (uint32_t)__popcll(cur.mask);
+                }
                 const int32_t k = (int32_t)(cur.kf & kCountMask) + (int32_t)__popcll(below);
                 int32_t pos = (cur.kf & (kNoneFlag | kSplitFlag)) ? -1 : cur.base + k;
                 if (cur.kf & kSplitFlag) pos = position_of(inst, rfirst[xi], rcnt[xi], cur.base + k);
-                if (STAGED) stage[valid ? off + k : sub] = (uint16_t)(i - begin);
-                else if (pos >= 0 && pos < N) src_out[pos] = (int32_t)i;
-                if (FULL || i < end) __builtin_nontemporal_store(pos, pos_out + i);
+                if (STAGED) stage[valid ? off + k : sub] = (uint16_t)o;
+                else if ((uint32_t)pos < (uint32_t)Ni) src_out[pos] = (int32_t)(begin + o);
+                if (FULL) __builtin_nontemporal_store(pos, pq + u * kWave);
+                else if (o < len) __builtin_nontemporal_store(pos, reinterpret_cast<int32_t *>(posb + (o << 2)));
                 wave_lds_fence();
             }
         }
@@ -340,13 +399,11 @@ __global__ __launch_bounds__(W *kWave) void dispatch_kernel(
         for (; g < end; g += U * kWave) group(g, std::false_type{});
     }
     if (STAGED) {
-        // staged slots in order, 64 per step: slot t belongs to the non-empty
-        // cell whose start is the last one at or before t; each expert's
-        // slots go to consecutive positions (per instance), so every store
-        // writes a few coalesced runs
+        // staged slots in order, 64 per step; each expert's slots go to
+        // consecutive positions (per instance), so every store writes a few
+        // coalesced runs
         constexpr int UF = 4;  // windows per step: their LDS reads overlap
-        const uint64_t upto = lane == kWave - 1 ? ~0ull : ((2ull << lane) - 1);
-        int cbase = -1;  // cells started before the current window, minus one
+        int cbase = 0;  // cells ended before the current window
         for (int w0 = 0; w0 < staged_pairs; w0 += UF * kWave) {
             uint64_t word[UF];
             int cb[UF];
@@ -360,25 +417,39 @@ __global__ __launch_bounds__(W *kWave) void dispatch_kernel(
                 cb[u] = cbase;
                 cbase += __popcll(word[u]);
             }
+            // slot t belongs to the c-th non-empty cell, c = the cells that
+            // end before t (those of earlier windows plus the end bits of
+            // lower lanes).  Every lane reads (a slot past the staged pairs
+            // reads a stale slot and cell ncells, whose entry is a valid
+            // expert), and only the store is conditional: reads under a
+            // branch each got a wait of their own.
             int e[UF];
-            uint16_t sidx[UF];
+            uint32_t sidx[UF];
 #pragma unroll
             for (int u = 0; u < UF; u++) {
                 const int t = w0 + u * kWave + lane;
-                e[u] = t < staged_pairs ? nel[cb[u] + __popcll(word[u] & upto)] : 0;
-                sidx[u] = t < staged_pairs ? stage[t] : 0;
+                const int ci = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(word[u] >> 32),
+                                                              __builtin_amdgcn_mbcnt_lo((uint32_t)word[u], (uint32_t)cb[u]));
+                e[u] = nel[ci];
+                sidx[u] = stage[(uint32_t)t < (uint32_t)sub ? t : sub];
+            }
+            int32_t cof[UF];
+            uint32_t ckf[UF];
+            int32_t cbase[UF];
+#pragma unroll
+            for (int u = 0; u < UF; u++) {
+                const uint2 t = inf[e[u]];
+                ckf[u] = t.x;
+                cbase[u] = (int32_t)t.y;
+                cof[u] = offs[e[u]];
             }
 #pragma unroll
             for (int u = 0; u < UF; u++) {
                 const int t = w0 + u * kWave + lane;
-                if (t < staged_pairs) {
-                    const Cell cell = cells[e[u]];
-                    const int32_t k = t - offs[e[u]];
-                    int32_t pos = -1;
-                    if (cell.kf & kSplitFlag) pos = position_of(inst, rfirst[e[u]], rcnt[e[u]], cell.base + k);
-                    else if (!(cell.kf & kNoneFlag)) pos = cell.base + k;
-                    if (pos >= 0 && pos < N) src_out[pos] = (int32_t)(begin + sidx[u]);
-                }
+                const int32_t k = t - cof[u];
+                int32_t pos = (ckf[u] & (kNoneFlag | kSplitFlag)) ? -1 : cbase[u] + k;
+                if (ckf[u] & kSplitFlag) pos = position_of(inst, rfirst[e[u]], rcnt[e[u]], cbase[u] + k);
+                if (t < staged_pairs && (uint32_t)pos < (uint32_t)Ni) src_out[pos] = (int32_t)(begin + sidx[u]);
             }
         }
     }
@@ -397,7 +468,7 @@ int pick_dispatch_waves(int E, int Phi, int64_t stage, bool pair) {
 }  // namespace
 
 size_t dispatch_lds_bytes(int E, int Phi, int waves, int64_t stage_pairs, bool pair) {
-    const size_t staged = stage_pairs > 0 ? (size_t)waves * ((size_t)stage_pairs / kWave * 8 + (size_t)E * 8 +
+    const size_t staged = stage_pairs > 0 ? (size_t)waves * ((size_t)stage_pairs / kWave * 8 + (size_t)E * 8 + 4 +
                                                              ((size_t)stage_pairs + kWave) * 2)
                                           : 0;
     return (size_t)waves * (E + 1) * (pair ? sizeof(Cell2) : sizeof(Cell1)) + (size_t)Phi * 8 +
