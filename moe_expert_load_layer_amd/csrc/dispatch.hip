@@ -31,11 +31,13 @@ namespace ep {
 namespace {
 
 // Per-expert state of a wave's sub-block (a "cell"): the bit mask of the
-// current 64-pair column, the count of the expert's pairs in earlier columns
-// with two flags in its top bits, and the position base: run + (off - Q) of
-// the one instance that takes all of the expert's pairs here, or the run
-// itself when a quota boundary falls inside (split), so that the k-th pair
-// of the cell goes to base + k, or to the instance a search of run + k finds.
+// current 64-pair column; kf, the cell's staging offset plus the count of the
+// expert's pairs in earlier columns, with two flags in its top bits; and
+// base, the position base plus that count: the base is run + (off - Q) of the
+// one instance that takes all of the expert's pairs here, or the run itself
+// when a quota boundary falls inside (split), so that the k-th pair of the
+// cell goes to base + k, or to the instance a search of run + k finds, and is
+// staged at off + k.
 // In LDS the fields live in separate arrays over the experts (masks, then
 // (count, base) pairs): the column's 8-byte mask accesses of neighbouring
 // experts then fall in neighbouring banks (with 16-byte cells the bank
@@ -86,9 +88,14 @@ __global__ __launch_bounds__(W *kWave) void dispatch_kernel(
     int32_t *soff = reinterpret_cast<int32_t *>(inst + Phi);                // [Phi + 1]
     int32_t *rfirst = soff + Phi + 1;                                       // [E]
     int32_t *rcnt = rfirst + E;                                             // [E]
-    int32_t *nel_all = rcnt + E;                                            // [W][E+1] if STAGED
-    int32_t *off_all = nel_all + (STAGED ? (size_t)W * (E + 1) : 0);        // [W][E] if STAGED
-    uint16_t *stage_all = reinterpret_cast<uint16_t *>(off_all + (STAGED ? (size_t)W * E : 0)); // [W][sub + 64]
+    // [W][E+1] if STAGED: per non-empty cell, in order, what the flush needs:
+    // (position - staged slot, 0), (run - staging offset, expert | split) or
+    // (0, none); aligned by an offset from the LDS base (an integer round
+    // trip of the pointer would lose its address space and turn every access
+    // into a flat one)
+    int2 *cinfo_all = reinterpret_cast<int2 *>(
+        sh_raw + ((reinterpret_cast<unsigned char *>(rcnt + E) - sh_raw + 7) & ~(ptrdiff_t)7));
+    uint16_t *stage_all = reinterpret_cast<uint16_t *>(cinfo_all + (STAGED ? (size_t)W * (E + 1) : 0)); // [W][sub + 64]
     // (the wave index is uniform in a wave: read into a scalar register, so
     // that the sub-block loop, its bounds and bases stay scalar)
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -172,10 +179,9 @@ __global__ __launch_bounds__(W *kWave) void dispatch_kernel(
     uint64_t *mk0 = cell_all + (size_t)wave * kCellWords * E1c;
     uint64_t *mk1 = mk0 + E1c;  // PAIR only
     uint2 *inf = reinterpret_cast<uint2 *>(mk0 + (size_t)(kCellWords - 1) * E1c);
-    int32_t *offs = off_all + (size_t)wave * (STAGED ? E : 0);  // staging offset of each cell
     uint16_t *stage = stage_all + (size_t)wave * sstride;
     uint64_t *sbits = sbits_all + (size_t)wave * nwords;   // bit t: staged slot t ends a cell
-    int32_t *nel = nel_all + (size_t)wave * (STAGED ? E + 1 : 0);  // non-empty cells' experts, in order
+    int2 *cinfo = cinfo_all + (size_t)wave * (STAGED ? E + 1 : 0);
     const SubPrefix pre = sub_prefix(ws, p, sb, nsb, sps, nseg, E1);
     int staged_pairs = 0;
     if (STAGED) {
@@ -214,14 +220,16 @@ __global__ __launch_bounds__(W *kWave) void dispatch_kernel(
             if (e < E) {
                 mk0[e] = 0ull;
                 if (PAIR) mk1[e] = 0ull;
-                inf[e] = make_uint2(flags, (uint32_t)base);
-                if (STAGED) offs[e] = off;
+                inf[e] = make_uint2((STAGED ? (uint32_t)off : 0u) | flags, (uint32_t)base);
             }
             if (STAGED) {
                 const bool full = e < E && cnt > 0;
                 const uint64_t fm = __ballot(full);
                 if (full) {
-                    nel[ncells + __popcll(fm & lanemask_lt())] = e;
+                    int2 ci = make_int2(base - off, 0);
+                    if (flags & kNoneFlag) ci = make_int2(0, (int32_t)kNoneFlag);
+                    else if (flags & kSplitFlag) ci = make_int2(base - off, e | (int32_t)kSplitFlag);
+                    cinfo[ncells + __popcll(fm & lanemask_lt())] = ci;
                     const int last = off + cnt - 1;
                     atomicOr(reinterpret_cast<unsigned long long *>(&sbits[last / kWave]),
                              1ull << (last % kWave));
@@ -232,7 +240,7 @@ __global__ __launch_bounds__(W *kWave) void dispatch_kernel(
         }
         // (uniform: the flush loop below then runs on scalar registers)
         staged_pairs = __builtin_amdgcn_readfirstlane(carry);
-        if (STAGED && lane == 0) nel[ncells] = 0;  // read by slots past the staged pairs
+        if (STAGED && lane == 0) cinfo[ncells] = make_int2(0, (int32_t)kNoneFlag);  // read by slots past the staged pairs
         if (lane == 0) {
             mk0[E] = 0ull;
             if (PAIR) mk1[E] = 0ull;
@@ -321,35 +329,35 @@ __global__ __launch_bounds__(W *kWave) void dispatch_kernel(
                     cb.kf = t.x;
                     cb.base = (int32_t)t.y;
                 }
-                const int32_t offa = STAGED ? offs[va ? ia : 0] : 0;
-                const int32_t offb = STAGED ? offs[vb ? ib : 0] : 0;
                 wave_lds_fence();
                 const uint64_t belowa = ca.mask & lt;
                 const uint64_t belowb = cb.mask1 & lt;
                 // one lane per expert of the pair: its lowest in the first column,
                 // else (absent there) its lowest in the second
                 if (belowa == 0) {
+                    const uint32_t n = (uint32_t)__popcll(ca.mask) + (uint32_t)__popcll(ca.mask1);
                     mk0[ia] = 0ull;
                     mk1[ia] = 0ull;
-                    inf[ia].x = ca.kf + (uint32_t)__popcll(ca.mask) + (uint32_t)__popcll(ca.mask1);
+                    inf[ia] = make_uint2(ca.kf + n, (uint32_t)ca.base + n);
                 }
                 if (cb.mask == 0 && belowb == 0) {
+                    const uint32_t n = (uint32_t)__popcll(cb.mask1);
                     mk1[ib] = 0ull;
-                    inf[ib].x = cb.kf + (uint32_t)__popcll(cb.mask1);
+                    inf[ib] = make_uint2(cb.kf + n, (uint32_t)cb.base + n);
                 }
-                const int32_t ka = (int32_t)(ca.kf & kCountMask) + (int32_t)__popcll(belowa);
-                const int32_t kb = (int32_t)(cb.kf & kCountMask) + (int32_t)__popcll(cb.mask) + (int32_t)__popcll(belowb);
-                auto place = [&](const Cell2 &c, int xi, bool valid, int32_t off, int32_t k, int col) {
+                const int32_t ka = (int32_t)__popcll(belowa);
+                const int32_t kb = (int32_t)__popcll(cb.mask) + (int32_t)__popcll(belowb);
+                auto place = [&](const Cell2 &c, int xi, bool valid, int32_t k, int col) {
                     const uint32_t o = go + (uint32_t)(col * kWave + lane);
                     int32_t pos = (c.kf & (kNoneFlag | kSplitFlag)) ? -1 : c.base + k;
                     if (c.kf & kSplitFlag) pos = position_of(inst, rfirst[xi], rcnt[xi], c.base + k);
-                    if (STAGED) stage[valid ? off + k : sub] = (uint16_t)o;
+                    if (STAGED) stage[valid ? (int32_t)(c.kf & kCountMask) + k : sub] = (uint16_t)o;
                     else if ((uint32_t)pos < (uint32_t)Ni) src_out[pos] = (int32_t)(begin + o);
                     if (FULL) __builtin_nontemporal_store(pos, pq + col * kWave);
                     else if (o < len) __builtin_nontemporal_store(pos, reinterpret_cast<int32_t *>(posb + (o << 2)));
                 };
-                place(ca, ia, va, offa, ka, u);
-                place(cb, ib, vb, offb, kb, u + 1);
+                place(ca, ia, va, ka, u);
+                place(cb, ib, vb, kb, u + 1);
                 wave_lds_fence();
             }
     
@@ -368,20 +376,18 @@ __global__ __launch_bounds__(W *kWave) void dispatch_kernel(
                     cur.kf = t.x;
                     cur.base = (int32_t)t.y;
                 }
-                // (read by every lane, the sink's lanes from cell 0: a read
-                // under a branch gets a wait of its own)
-                const int32_t off = STAGED ? offs[valid ? xi : 0] : 0;
                 wave_lds_fence();
                 const uint32_t o = go + (uint32_t)(u * kWave + lane);
                 const uint64_t below = cur.mask & lt;
                 if (below == 0) {
+                    const uint32_t n = (uint32_t)__popcll(cur.mask);
                     mk0[xi] = 0ull;
-                    inf[xi].x = cur.kf + (uint32_t)__popcll(cur.mask);
+                    inf[xi] = make_uint2(cur.kf + n, (uint32_t)cur.base + n);
                 }
-                const int32_t k = (int32_t)(cur.kf & kCountMask) + (int32_t)__popcll(below);
+                const int32_t k = (int32_t)__popcll(below);
                 int32_t pos = (cur.kf & (kNoneFlag | kSplitFlag)) ? -1 : cur.base + k;
                 if (cur.kf & kSplitFlag) pos = position_of(inst, rfirst[xi], rcnt[xi], cur.base + k);
-                if (STAGED) stage[valid ? off + k : sub] = (uint16_t)o;
+                if (STAGED) stage[valid ? (int32_t)(cur.kf & kCountMask) + k : sub] = (uint16_t)o;
                 else if ((uint32_t)pos < (uint32_t)Ni) src_out[pos] = (int32_t)(begin + o);
                 if (FULL) __builtin_nontemporal_store(pos, pq + u * kWave);
                 else if (o < len) __builtin_nontemporal_store(pos, reinterpret_cast<int32_t *>(posb + (o << 2)));
@@ -423,32 +429,25 @@ __global__ __launch_bounds__(W *kWave) void dispatch_kernel(
             // reads a stale slot and cell ncells, whose entry is a valid
             // expert), and only the store is conditional: reads under a
             // branch each got a wait of their own.
-            int e[UF];
+            int2 ci[UF];
             uint32_t sidx[UF];
 #pragma unroll
             for (int u = 0; u < UF; u++) {
                 const int t = w0 + u * kWave + lane;
-                const int ci = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(word[u] >> 32),
-                                                              __builtin_amdgcn_mbcnt_lo((uint32_t)word[u], (uint32_t)cb[u]));
-                e[u] = nel[ci];
+                const int c = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(word[u] >> 32),
+                                                             __builtin_amdgcn_mbcnt_lo((uint32_t)word[u], (uint32_t)cb[u]));
+                ci[u] = cinfo[c];
                 sidx[u] = stage[(uint32_t)t < (uint32_t)sub ? t : sub];
-            }
-            int32_t cof[UF];
-            uint32_t ckf[UF];
-            int32_t cbase[UF];
-#pragma unroll
-            for (int u = 0; u < UF; u++) {
-                const uint2 t = inf[e[u]];
-                ckf[u] = t.x;
-                cbase[u] = (int32_t)t.y;
-                cof[u] = offs[e[u]];
             }
 #pragma unroll
             for (int u = 0; u < UF; u++) {
                 const int t = w0 + u * kWave + lane;
-                const int32_t k = t - cof[u];
-                int32_t pos = (ckf[u] & (kNoneFlag | kSplitFlag)) ? -1 : cbase[u] + k;
-                if (ckf[u] & kSplitFlag) pos = position_of(inst, rfirst[e[u]], rcnt[e[u]], cbase[u] + k);
+                const uint32_t f = (uint32_t)ci[u].y;
+                int32_t pos = (f & kNoneFlag) ? -1 : ci[u].x + t;
+                if (f & kSplitFlag) {
+                    const int ex = (int)(f & kCountMask);
+                    pos = position_of(inst, rfirst[ex], rcnt[ex], pos);
+                }
                 if (t < staged_pairs && (uint32_t)pos < (uint32_t)Ni) src_out[pos] = (int32_t)(begin + sidx[u]);
             }
         }
@@ -468,8 +467,8 @@ int pick_dispatch_waves(int E, int Phi, int64_t stage, bool pair) {
 }  // namespace
 
 size_t dispatch_lds_bytes(int E, int Phi, int waves, int64_t stage_pairs, bool pair) {
-    const size_t staged = stage_pairs > 0 ? (size_t)waves * ((size_t)stage_pairs / kWave * 8 + (size_t)E * 8 + 4 +
-                                                             ((size_t)stage_pairs + kWave) * 2)
+    const size_t staged = stage_pairs > 0 ? (size_t)waves * ((size_t)stage_pairs / kWave * 8 + (size_t)E * 8 + 8 +
+                                                             ((size_t)stage_pairs + kWave) * 2) + 8
                                           : 0;
     return (size_t)waves * (E + 1) * (pair ? sizeof(Cell2) : sizeof(Cell1)) + (size_t)Phi * 8 +
            (size_t)(Phi + 1) * 4 + (size_t)E * 8 + staged;
