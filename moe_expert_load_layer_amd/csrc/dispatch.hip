@@ -174,7 +174,16 @@ __global__ __launch_bounds__(W *kWave) void dispatch_kernel(
 
     // each wave walks the plan's sub-blocks with a stride of the plan's waves,
     // reusing the block's route table; no block barriers below
-    for (int64_t sb = (int64_t)blockIdx.x * W + wave; sb < nsb; sb += (int64_t)gridDim.x * W) {
+    // workgroups go to the 8 XCDs round-robin: the ones on one XCD take
+    // consecutive sub-blocks, so that the runs of neighbouring sub-blocks in
+    // dispatch_src meet in one L2
+    int64_t lblk;
+    {
+        const int nb = (int)gridDim.x, x = (int)blockIdx.x;
+        const int q = nb / 8, r = nb % 8, c = x % 8, j = x / 8;
+        lblk = c < r ? (int64_t)c * (q + 1) + j : (int64_t)r * (q + 1) + (int64_t)(c - r) * q + j;
+    }
+    for (int64_t sb = lblk * W + wave; sb < nsb; sb += (int64_t)gridDim.x * W) {
     wave_lds_fence();  // the previous sub-block's reads of the wave's LDS are done
     uint64_t *mk0 = cell_all + (size_t)wave * kCellWords * E1c;
     uint64_t *mk1 = mk0 + E1c;  // PAIR only
