@@ -403,6 +403,8 @@ __global__ __launch_bounds__(kWave) void plan_kernel_lanes(const int32_t *__rest
     const bool bad_load = __ballot(lneg) != 0 || readlane_i64(wave_incl_scan_i64(lsum), kWave - 1) > 0x7fffffffLL;
     __syncthreads();
 
+    // lane i: floor((2^32 - 1) / (i + 1)), for the water-fill's division by m*
+    const uint32_t rcp_m = 0xffffffffu / (uint32_t)(lane + 1);
     const int cap = 2 * S + R;
     int steps = 0, cap_hit = 0;
     for (; !bad_load;) {
@@ -581,8 +583,16 @@ __global__ __launch_bounds__(kWave) void plan_kernel_lanes(const int32_t *__rest
                 if (mstar > 0) {
                     const int ls = __ffsll((long long)__ballot(act && pos == mstar - 1)) - 1;
                     const uint32_t Ss = (uint32_t)__builtin_amdgcn_readlane((int)Sinc, ls);
-                    const uint32_t base = Ss / (uint32_t)mstar;
-                    const uint32_t rem = Ss - (uint32_t)mstar * base;
+                    // Ss / m* from the reciprocal held by lane m* - 1: the
+                    // high word of Ss * floor((2^32 - 1) / m*) is the
+                    // quotient or one less (Ss < 2^32), one step corrects it
+                    const uint32_t um = (uint32_t)mstar;
+                    uint32_t base = __umulhi(Ss, (uint32_t)__builtin_amdgcn_readlane((int)rcp_m, mstar - 1));
+                    uint32_t rem = Ss - um * base;
+                    if (rem >= um) {
+                        base += 1;
+                        rem -= um;
+                    }
                     if (act && pos < mstar) qn = (int)base - b + ((uint32_t)pos < rem ? 1 : 0);
                 }
                 const int newLh = __builtin_amdgcn_readlane(act ? b + qn : rl, h);
