@@ -9,11 +9,11 @@
 //
 // One wave per sub-block (the histogram's); each workgroup builds the plan's
 // route table (slot offsets, per-instance (end, off - Q)) once and its waves
-// then walk one or more sub-blocks (see the launcher).  Every pair needs its rank among the pairs of
-// its expert, so each 64-pair column is ranked with an LDS bit mask per
-// expert (each lane ORs its bit, counts the bits below it) plus a per-expert
-// running count; the first rank of the expert in the sub-block comes from the
-// histogram's workspace rows.  Positions are unique, so the writes of
+// then walk one or more sub-blocks (see the launcher).  Every pair needs its
+// rank among the pairs of its expert, so each 64-pair column is ranked with an
+// LDS bit mask per expert (each lane ORs its bit, counts the bits below it)
+// plus a per-expert running count; the first rank of the expert in the
+// sub-block comes from the histogram's workspace rows.  Positions are unique, so the writes of
 // dispatch_src never collide.
 //
 // dispatch_src is written through LDS when the staging buffer leaves enough
@@ -40,9 +40,10 @@ namespace {
 // staged at off + k.
 // In LDS the fields live in separate arrays over the experts (masks, then
 // (count, base) pairs): the column's 8-byte mask accesses of neighbouring
-// experts then fall in neighbouring banks (with 16-byte cells the bank
-// conflicts were 45 % higher and the Qwen3-like batch 2-8 % slower).  These
-// structs hold one cell's values in registers.
+// experts then fall in neighbouring banks (with 16-byte cells the
+// Qwen3-like batch took 1.8 times the bank-conflict cycles, and the staged
+// batches ran 2-8 % slower).  These structs hold one cell's values in
+// registers.
 struct Cell1 {
     uint64_t mask;
     uint32_t kf;
