@@ -34,7 +34,7 @@ from the mean launch time measured with HIP events on the stream the fills run
 on.  `traffic` is the HBM bytes per launch from the rocprofv3 FETCH_SIZE and
 WRITE_SIZE summary committed for this kernel source (null when the source has
 changed since).  The `workloads` object repeats the measurement, compactly, for
-every workload.  The CPU baseline times the C oracle on a bounded sample of the
+every workload, with the dispatch layout over all plans beside it.  The CPU baseline times the C oracle on a bounded sample of the
 same layers on the host (hist + plan + reroute, and the slot fill as memcpy).
 """
 from __future__ import annotations
@@ -218,8 +218,9 @@ def cpu_slot_fill(weights: torch.Tensor, phy2log_host: np.ndarray, wl, budget_s:
 
 def workload_summary(name: str, dev, cpu_bound: bool, fill_layers: int = 16):
     """Compact numbers for one workload at full size: the path (fastest of one
-    stream and two chunks), each kernel alone, single-layer latencies, the slot
-    fill over its first layers, and the balance."""
+    stream and two chunks), each kernel alone, single-layer latencies, the
+    dispatch layout over all plans, the slot fill over its first layers, and the
+    balance."""
     wl = W.get(name)
     P, N, E, S = wl.num_plans, wl.pairs_per_plan, wl.num_experts, wl.num_spare
     ids = W.make_ids(wl, device=dev)
@@ -263,6 +264,12 @@ def workload_summary(name: str, dev, cpu_bound: bool, fill_layers: int = 16):
     t_plan = timed(lambda: ep.ep_plan_quota(load, lay, out=plan, status=status))
     t_rr = timed(lambda: ep.ep_reroute(ids, lay, plan.phy_quota, plan.log2phy, plan.logcnt, ws, phys_ids=phys))
     serial()
+    soff = torch.empty((P, lay.num_phys + 1), dtype=torch.int32, device=dev)
+    dpos = torch.empty_like(ids)
+    dsrc = torch.empty_like(ids)
+    t_disp = timed(lambda: ep.ep_dispatch_layout(ids, lay, plan.phy_quota, plan.log2phy, plan.logcnt, ws,
+                                                 slot_offsets=soff, dispatch_pos=dpos, dispatch_src=dsrc), reps=3)
+    del soff, dpos, dsrc
     ids1, load1 = ids[:1], load[:1].clone()
     pl1 = ep.alloc_plan(1, lay, dev)
     t_plan1 = timed(lambda: ep.ep_plan_quota(load1, lay, out=pl1), reps=15) * 1e3
@@ -296,6 +303,8 @@ def workload_summary(name: str, dev, cpu_bound: bool, fill_layers: int = 16):
         "hist_moved_frac": kern["per_kernel"]["hist_moved_frac"],
         "reroute_moved_frac": kern["per_kernel"]["reroute_moved_frac"],
         "plan_us_per_layer_batched": t_plan * 1e3 / P, "plan_us_single_layer": t_plan1,
+        "dispatch_layout_ms": t_disp,
+        "dispatch_layout_12B_frac": 12.0 * P * N / (t_disp * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "imbalance_before_mean": float(imb_np[:, 0].mean()),
         "imbalance_after_mean": float(imb_np[:, 1].mean()),
         "imbalance_after_max": float(imb_np[:, 1].max()),
@@ -701,6 +710,8 @@ def main(argv=None) -> int:
             "hist_moved_frac": kern["per_kernel"]["hist_moved_frac"],
             "reroute_moved_frac": kern["per_kernel"]["reroute_moved_frac"],
             "plan_us_per_layer_batched": ph_plan * 1e3 / P, "plan_us_single_layer": lat_plan,
+            "dispatch_layout_ms": disp_ms,
+            "dispatch_layout_12B_frac": next_rows["dispatch_layout_GBps"] / HBM_PEAK_GBPS,
             "fill_ms_per_layer": fill["ms"], "fill_frac": fill["frac"], "fill_moved_frac": fill["moved_frac"],
             "fill_layers": P, "filled_slots_mean": fill["filled"], "distinct_experts_mean": fill["distinct"],
             "imbalance_before_mean": out["balance"]["imbalance_before_mean"],
