@@ -428,8 +428,8 @@ __global__ __launch_bounds__(W *kWave) void dispatch_kernel(
             int cb[UF];
 #pragma unroll
             for (int u = 0; u < UF; u++) {
-                const int64_t wi = w0 / kWave + u;
-                word[u] = wi < nwords ? sbits[wi] : 0ull;
+                const int wi = w0 / kWave + u;  // (32-bit: a scalar compare)
+                word[u] = wi < (int)nwords ? sbits[wi] : 0ull;
             }
 #pragma unroll
             for (int u = 0; u < UF; u++) {
@@ -461,7 +461,8 @@ __global__ __launch_bounds__(W *kWave) void dispatch_kernel(
                     const int ex = (int)(f & kCountMask);
                     pos = position_of(inst, rfirst[ex], rcnt[ex], pos);
                 }
-                if (t < staged_pairs && (uint32_t)pos < (uint32_t)Ni) src_out[pos] = (int32_t)(begin + sidx[u]);
+                // (a slot past the staged pairs reads record ncells, "none")
+                if ((uint32_t)pos < (uint32_t)Ni) src_out[pos] = (int32_t)(begin + sidx[u]);
             }
         }
     }
