@@ -141,9 +141,9 @@ __global__ __launch_bounds__(kHistWaves * kWave) void hist_kernel(
     }
 }
 
-constexpr int kScanWaves = 4;  // small workgroups start on a CU busy with other kernels
 constexpr int kScanUnroll = 8;
 
+template <int kScanWaves>
 __global__ __launch_bounds__(kScanWaves * kWave) void scan_kernel(
     int32_t *__restrict__ ws, int64_t nsb, int64_t nseg, int32_t E, int32_t *__restrict__ load,
     uint32_t *__restrict__ status) {
@@ -215,9 +215,15 @@ hipError_t launch_histogram(const int32_t *ids, int64_t N, int32_t P, int32_t E,
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
-    dim3 g2((unsigned)((E + 1 + kWave - 1) / kWave), (unsigned)P);
-    hipLaunchKernelGGL(scan_kernel, g2, dim3(kScanWaves * kWave), 0, s, ws, g.nsb, g.nseg, E, load,
-                       status);
+    // 4-wave workgroups start on CUs busy with other kernels (a concurrent
+    // reroute); a launch of a few plans with many segments gets 16 waves per
+    // column block, each scanning a quarter of the segments a 4-wave one would
+    const unsigned cb = (unsigned)((E + 1 + kWave - 1) / kWave);
+    dim3 g2(cb, (unsigned)P);
+    if ((int64_t)cb * P <= 16 && g.nseg >= 128)
+        hipLaunchKernelGGL(scan_kernel<16>, g2, dim3(16 * kWave), 0, s, ws, g.nsb, g.nseg, E, load, status);
+    else
+        hipLaunchKernelGGL(scan_kernel<4>, g2, dim3(4 * kWave), 0, s, ws, g.nsb, g.nseg, E, load, status);
     return hipGetLastError();
 }
 
