@@ -13,7 +13,10 @@ Inputs are synthetic, seeded, and resident in HBM before timing starts.
 
 value = (token,k) pairs per second through hist + plan + reroute (HIP events
 around that phase in every timed step); ms_per_step is the whole step
-including the slot fills and statistics.
+including the slot fills and statistics.  The `kernels` object also carries
+single-layer latencies: each kernel alone, and the whole chain of one layer in
+one call on one stream (`route_chain_us_single_layer`), the latency a forward
+pass that plans layer by layer sees.
 
 Byte rules (algorithmic bytes per unit of work):
   path        12 B per pair: the ID read by the histogram (4), read again and the
@@ -553,6 +556,11 @@ def main(argv=None) -> int:
     lat_plan = lat(lambda: ep.ep_plan_quota(load1, lay, out=pl1), args.latency_reps)
     lat_rr = lat(lambda: ep.ep_reroute(ids1, lay, pl1.phy_quota, pl1.log2phy, pl1.logcnt, ws1, phys_ids=ph1),
                  args.latency_reps)
+    # the whole chain for one layer in one call on one stream, as a forward pass
+    # without batching runs it (histogram, scan, planner, reroute and the gaps
+    # between their launches)
+    ld1c, st1c, pl1c, ph1c = load1.clone(), st1.clone(), ep.alloc_plan(1, lay, dev), torch.empty_like(ids1)
+    lat_chain = lat(lambda: ep.ep_route_noalloc(ids1, lay, ld1c, st1c, pl1c, ph1c), args.latency_reps)
 
     # next rows beyond the timed step, one launch over all plans each
     slot_off = torch.empty((P, lay.num_phys + 1), dtype=torch.int32, device=dev)
@@ -634,7 +642,8 @@ def main(argv=None) -> int:
                     "plan_us_per_layer_batched": ph_plan * 1e3 / P,
                     "plan_us_single_layer": lat_plan,
                     "hist_us_single_layer": lat_hist,
-                    "reroute_us_single_layer": lat_rr},
+                    "reroute_us_single_layer": lat_rr,
+                    "route_chain_us_single_layer": lat_chain},
         "next_rows": next_rows,
         "balance": {
             "imbalance_before_mean": float(imb_np[:, 0].mean()),
